@@ -1,0 +1,279 @@
+"""Benchmark of the causal GQA + RoPE path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  prefill phase  (24 query / 8 KV heads, head dim 128, batch 8 x 2048 tokens):
+                 RoPE on q and k, cache append, causal GQA prefill;
+  decode phase   (64 sequences, cache lengths uniform on {256..2048}, same
+                 heads): 32 generation steps of RoPE on the new q and k,
+                 cache append, length update and cached GQA decode.
+`value` is the decode phase's KV-read rate (cache bytes every decode call
+must read / decode-phase time, GB/s); the prefill phase's attention rate is
+reported beside it (TFLOP/s over unmasked query-key pairs).  Both are also
+given per kernel against the MI355X peaks (HBM 8 TB/s; dense bf16 MFMA
+2.5 PFLOP/s), from HIP events recorded on the stream the kernels run on.
+The fp64 CPU oracle is timed on a bounded sample of the same decode workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GQA decode KV-read GB/s + prefill attn TFLOP/s, % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    return ap.parse_args()
+
+
+def kernel_sha(name):
+    with open(os.path.join(ROOT, "rope_gqa_causal_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kind, src, launches_bytes):
+    """HBM bytes per launch from committed counter runs, if the kernel is unchanged."""
+    path = os.path.join(PROFILES, f"counters_{kind}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("kernel_sha") != kernel_sha(src):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+class Prefill:
+    def __init__(self, rgc, synth):
+        w = synth.WORKLOADS["prefill3p8b"]
+        self.w = w
+        g = synth.generator(w.seed)
+        q, k, v = synth.qkv(w.B, w.S, w.Hq, w.Hkv, w.D, g, w.dtype)
+        self.q, self.k, self.v = q.cuda(), k.cuda(), v.cuda()
+        self.kc = torch.empty((w.B, w.Hkv, w.S, w.D), dtype=w.dtype, device="cuda")
+        self.vc = torch.empty_like(self.kc)
+        self.o = torch.empty_like(self.q)
+        self.pos0 = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+        self.rgc = rgc
+        self.flops = 4.0 * w.D * w.B * w.Hq * w.S * (w.S + 1) / 2  # unmasked pairs x 4D
+        self.events = []
+
+    def run(self, record):
+        r = self.rgc
+        r.rope_apply(self.q, self.pos0)
+        r.rope_apply(self.k, self.pos0)
+        r.kv_cache_append(self.kc, self.vc, self.k, self.v, self.pos0)
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        r.gqa_attn_prefill(self.q, self.kc, self.vc, self.pos0, out=self.o)
+        if record:
+            e1.record()
+            self.events.append((e0, e1))
+
+
+class Decode:
+    def __init__(self, rgc, synth):
+        w = synth.WORKLOADS["ragged_decode"]
+        self.w = w
+        g = synth.generator(w.seed)
+        self.lens0_cpu = synth.lengths(w.B, w.len_lo, w.len_hi, g)
+        self.S_max = w.len_hi + w.steps
+        kc, vc = synth.filled_cache(w.B, w.Hkv, self.S_max, w.D, g, w.dtype)
+        self.kc_cpu, self.vc_cpu = kc, vc
+        self.kc, self.vc = kc.cuda(), vc.cuda()
+        q, k, v = synth.qkv(w.B * w.steps, 1, w.Hq, w.Hkv, w.D, g, w.dtype)
+        self.q = q.view(w.steps, w.B, 1, w.Hq, w.D).cuda()
+        self.k = k.view(w.steps, w.B, 1, w.Hkv, w.D).cuda()
+        self.v = v.view(w.steps, w.B, 1, w.Hkv, w.D).cuda()
+        self.lens0 = self.lens0_cpu.cuda()
+        self.lens = self.lens0.clone()
+        self.o = torch.empty((w.B, w.Hq, w.D), dtype=w.dtype, device="cuda")
+        self.ws = rgc.decode_workspace(w.B, w.Hq, w.Hkv, w.D, self.S_max)
+        self.rgc = rgc
+        # KV bytes the t-th decode call must read: every cached row of every
+        # sequence, new token included (lengths lens0 + t + 1).
+        per_token = w.Hkv * w.D * 2 * 2
+        self.bytes_per_call = [per_token * float((self.lens0_cpu + t + 1).sum()) for t in range(w.steps)]
+        self.events = []
+
+    def run(self, record):
+        r, w = self.rgc, self.w
+        self.lens.copy_(self.lens0)
+        for t in range(w.steps):
+            r.rope_apply(self.q[t], self.lens)
+            r.rope_apply(self.k[t], self.lens)
+            r.kv_cache_append(self.kc, self.vc, self.k[t], self.v[t], self.lens)
+            self.lens += 1
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            r.gqa_attn_decode(self.q[t][:, 0], self.kc, self.vc, self.lens, self.S_max, self.ws,
+                              out=self.o)
+            if record:
+                e1.record()
+                self.events.append((t, e0, e1))
+
+
+def cpu_baseline(dec, seconds):
+    """Time the fp64 oracle's decode on the host over whole decode calls."""
+    import oracle
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", threads))
+    w = dec.w
+    q = dec.q.cpu()
+    lens = dec.lens0_cpu.clone()
+    done_bytes, t_total, calls = 0.0, 0.0, 0
+    while calls < w.steps and (calls == 0 or t_total < seconds):
+        lens += 1
+        t0 = time.perf_counter()
+        oracle.attn_decode(q[calls][:, 0], dec.kc_cpu, dec.vc_cpu, lens, nthreads=threads)
+        t_total += time.perf_counter() - t0
+        done_bytes += dec.bytes_per_call[calls]
+        calls += 1
+    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} of the {w.steps} decode calls of the ragged-decode workload "
+                      f"(64 sequences, all heads), fp64, {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import rope_gqa_causal_amd as rgc
+    from rope_gqa_causal_amd import synth
+
+    print("[bench] setting up inputs", file=sys.stderr, flush=True)
+    pre = Prefill(rgc, synth)
+    dec = Decode(rgc, synth)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        pre.run(False)
+        dec.run(False)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    phase = []
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        a = torch.cuda.Event(enable_timing=True)
+        m = torch.cuda.Event(enable_timing=True)
+        z = torch.cuda.Event(enable_timing=True)
+        a.record()
+        pre.run(True)
+        m.record()
+        dec.run(True)
+        z.record()
+        phase.append((a, m, z))
+    t_end.record()
+    torch.cuda.synchronize()
+    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+
+    total_ms = t_start.elapsed_time(t_end)
+    pre_ms = sum(a.elapsed_time(m) for a, m, _ in phase)
+    dec_ms = sum(m.elapsed_time(z) for _, m, z in phase)
+    dec_bytes = sum(dec.bytes_per_call) * args.steps
+    value = dec_bytes / (dec_ms * 1e-3) / 1e9
+    prefill_tflops = pre.flops * args.steps / (pre_ms * 1e-3) / 1e12
+
+    # Per-launch kernel durations (HIP events around each call).
+    pk_ms = [e0.elapsed_time(e1) for e0, e1 in pre.events]
+    dk = [(t, e0.elapsed_time(e1)) for t, e0, e1 in dec.events]
+    pk_avg = sum(pk_ms) / len(pk_ms)
+    dk_avg = sum(ms for _, ms in dk) / len(dk)
+    dk_bytes_avg = sum(dec.bytes_per_call[t] for t, _ in dk) / len(dk)
+    dec_achieved = dk_bytes_avg / (dk_avg * 1e-3) / 1e9
+    pre_achieved = pre.flops / (pk_avg * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill 3.8B-shaped (B8 x 2048, 24q/8kv, D128) + ragged decode "
+                        "(64 seqs, L~U{256..2048}, 24q/8kv, D128, 32 steps); bf16, fp32 accumulate",
+            "global_batch": dec.w.B,
+            "seq_len": pre.w.S,
+            "parallelism": "single GPU",
+        },
+        "prefill": {
+            "tflops": round(prefill_tflops, 2),
+            "phase_ms_per_step": round(pre_ms / args.steps, 4),
+            "note": "RoPE q,k + append + causal prefill; FLOPs count unmasked pairs x 4D",
+        },
+        "decode_phase_ms_per_step": round(dec_ms / args.steps, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gqa_attn_decode (split-K + combine)",
+            "achieved": round(dec_achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_achieved / HBM_PEAK_GBS, 4),
+            "traffic": stored_traffic("decode", "decode.hip", dk_bytes_avg),
+            "algorithmic_bytes_per_launch": round(dk_bytes_avg),
+            "avg_launch_us": round(dk_avg * 1e3, 3),
+        },
+        "roofline_prefill": {
+            "bound": "mfma",
+            "kernel": "gqa_attn_prefill",
+            "achieved": round(pre_achieved, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre_achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": stored_traffic("prefill", "prefill.hip", None),
+            "algorithmic_flops_per_launch": pre.flops,
+            "avg_launch_us": round(pk_avg * 1e3, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * rgc.h -- C ABI of the MI355X (gfx950) library for causal grouped-query
+ * attention with rotary position embedding over a key/value cache.
+ *
+ * The operations, and the pages that define them (cited by title and
+ * section):
+ *  - RoPE on q and k: page "750美元从零训练3个LLM：一位开发者的实战复盘"
+ *    (kongchang.com), section "V1：现代架构基线"; page "从零手训LLaMa：125M
+ *    模型11小时训练全记录" (kongchang.com), section "核心架构：手动实现LLaMa的
+ *    四个关键组件" (RoPE as a rotation matrix).
+ *  - KV cache append and cached decode: the first page, section
+ *    "V3：扩容与推理优化"; the second page, the KV cache paragraph of the
+ *    core-architecture section.
+ *  - Grouped-query attention: the first page, section "V2：引入前沿技术";
+ *    the second page, core-architecture section; page "训练3.8B LLM至0.384
+ *    CORE，成本998美元 – Hugo Vergnes", section "设置" (24 query / 8 KV
+ *    heads).
+ *  - Causal attention with the diagonal included: the 3.8B page, section
+ *    "无效的方法"; the m.nxbn.cn build-an-LLM page, section 3.1.
+ *  - Differential attention: the first page, section "V2：引入前沿技术".
+ *
+ * Conventions shared by every entry point:
+ *  - Every data pointer is a DEVICE pointer (HIP global memory) unless the
+ *    argument says "host".  The caller owns every buffer; the library never
+ *    allocates, frees or synchronises and keeps no mutable global state.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns.
+ *  - Shapes are element counts; strides are in ELEMENTS, not bytes.  The
+ *    head-dimension stride is always 1.
+ *  - dtype is RGC_F32 or RGC_BF16 and applies to every floating-point tensor
+ *    of the call except lse (always fp32).
+ *  - Base pointers must be 16-byte aligned and every stride a multiple of
+ *    16 bytes' worth of elements (8 for bf16, 4 for fp32), so that rows load
+ *    as 16-byte vectors; otherwise RGC_ERR_LAYOUT.
+ *  - All arguments are checked on the host before anything is enqueued; a
+ *    negative status means nothing was launched.  B == 0 or an empty
+ *    sequence dimension is a successful no-op.
+ *  - Facts only the device can see (a slot or length held in a device
+ *    array that falls outside the cache) never cause an out-of-bounds
+ *    access: the affected rows are skipped (append) or written as NaN
+ *    (attention), and 1 is stored to *err_flag when err_flag is not NULL.
+ *    The library never clears err_flag.
+ *  - Query head h reads KV head h / (Hq / Hkv); Hq must be a multiple of
+ *    Hkv (RGC_ERR_GROUP otherwise).
+ *  - Supported head dims: 32, 64, 128 (RGC_ERR_HEADDIM otherwise).
+ */
+#ifndef RGC_H
+#define RGC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RGC_ABI_VERSION 1
+
+typedef enum { RGC_F32 = 0, RGC_BF16 = 1 } rgc_dtype;
+
+typedef enum {
+  RGC_OK = 0,
+  RGC_ERR_NULL = -1,      /* a required pointer is NULL                      */
+  RGC_ERR_SHAPE = -2,     /* a negative or inconsistent size                 */
+  RGC_ERR_GROUP = -3,     /* Hq is not a multiple of Hkv                     */
+  RGC_ERR_DTYPE = -4,     /* dtype is neither RGC_F32 nor RGC_BF16           */
+  RGC_ERR_HEADDIM = -5,   /* head dim not supported                          */
+  RGC_ERR_LAYOUT = -6,    /* misaligned pointer or stride                    */
+  RGC_ERR_CAPACITY = -7,  /* a host-known length exceeds the cache           */
+  RGC_ERR_WORKSPACE = -8, /* workspace missing or too small                  */
+  RGC_ERR_HIP = -9,       /* the HIP runtime refused a launch                */
+  RGC_ERR_ARG = -10       /* any other invalid argument                      */
+} rgc_status;
+
+typedef enum {
+  RGC_ROPE_HALF = 0,       /* pairs (x_i, x_{i+D/2}), i < D/2                */
+  RGC_ROPE_INTERLEAVED = 1 /* pairs (x_{2i}, x_{2i+1})                        */
+} rgc_rope_style;
+
+/* ABI version of the loaded library (RGC_ABI_VERSION at build time). */
+int rgc_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* rgc_status_string(int status);
+
+/*
+ * rgc_rope_apply -- rotary position embedding, in place.
+ *   x     [B,S,H,D] of dtype, strides (sb, ss, sh); rotated in place.
+ *   pos0  [B] int32 or NULL (all zero): token (b, s) sits at position
+ *         pos0[b] + s.
+ *   base  frequency base (10000 in the pages' models); theta_i =
+ *         base^(-2i/D) for pair i < D/2.
+ *   style RGC_ROPE_HALF or RGC_ROPE_INTERLEAVED.
+ * Each pair (a, b) becomes (a cos t - b sin t, a sin t + b cos t) with
+ * t = position * theta_i.  The angle is formed and reduced modulo 2*pi in
+ * fp64; sine, cosine and the rotation run in fp32; bf16 results are rounded
+ * to nearest even.  Apply to q and to k, never to v.  D may be any even
+ * size from 2 to 256 here.
+ */
+int rgc_rope_apply(void* x, int dtype, int B, int S, int H, int D, int64_t sb,
+                   int64_t ss, int64_t sh, const int32_t* pos0, double base,
+                   int style, void* stream);
+
+/*
+ * rgc_kv_cache_append -- copy new key and value rows into the caches.
+ *   k_cache, v_cache  [B,Hkv,S_max,D] of dtype, strides (c_sb, c_sh, c_ss)
+ *                     shared by both caches.
+ *   k_new, v_new      [B,S_new,Hkv,D] of dtype, strides (sb, ss, sh) shared
+ *                     by both.
+ *   pos0              [B] int32, the first slot written for sequence b
+ *                     (normally its current length).
+ * cache[b, h, pos0[b] + s, :] = new[b, s, h, :], bit for bit.  Rows whose
+ * slot falls outside [0, S_max) are skipped and flagged in *err_flag.  The
+ * library never updates lengths: the caller advances its length array after
+ * the append, on the same stream.  Store keys after RoPE (the cache holds
+ * rotated keys and raw values).
+ */
+int rgc_kv_cache_append(void* k_cache, void* v_cache, int dtype, int B,
+                        int Hkv, int D, int S_max, int64_t c_sb, int64_t c_sh,
+                        int64_t c_ss, const void* k_new, const void* v_new,
+                        int S_new, int64_t sb, int64_t ss, int64_t sh,
+                        const int32_t* pos0, int32_t* err_flag, void* stream);
+
+/*
+ * rgc_gqa_attn_prefill -- causal GQA attention of a block of query rows over
+ * the cache.
+ *   o        [B,Sq,Hq,D] of dtype, strides (o_sb, o_ss, o_sh); written.
+ *   q        [B,Sq,Hq,D] of dtype, strides (q_sb, q_ss, q_sh); already
+ *            rotated.
+ *   k_cache, v_cache  [B,Hkv,S_max,D], strides (kv_sb, kv_sh, kv_ss); a
+ *            [B,S,Hkv,D] tensor stands in for a cache with kv_sb = S*Hkv*D,
+ *            kv_sh = D, kv_ss = Hkv*D.
+ *   q_start  [B] int32 or NULL (all zero): row s of sequence b sits at slot
+ *            p = q_start[b] + s and attends to slots 0..p inclusive.
+ *   scale    softmax scale (normally 1/sqrt(D)).
+ *   lse      [B,Hq,Sq] fp32 contiguous or NULL: log-sum-exp of the scaled
+ *            scores (natural log).
+ * o[b,s,h,:] = sum_{j<=p} softmax_j(scale * q . K_j) V_j with KV head
+ * h / (Hq/Hkv).  bf16: scores, softmax and accumulation in fp32, the
+ * probabilities rounded to bf16 for the second product, the output rounded
+ * to nearest even.  A sequence whose q_start puts a row outside [0, S_max)
+ * gets NaN rows and a flag.
+ */
+int rgc_gqa_attn_prefill(void* o, const void* q, const void* k_cache,
+                         const void* v_cache, int dtype, int B, int Sq, int Hq,
+                         int Hkv, int D, int S_max, int64_t q_sb, int64_t q_ss,
+                         int64_t q_sh, int64_t o_sb, int64_t o_ss,
+                         int64_t o_sh, int64_t kv_sb, int64_t kv_sh,
+                         int64_t kv_ss, const int32_t* q_start, float scale,
+                         float* lse, int32_t* err_flag, void* stream);
+
+/*
+ * Bytes of device workspace rgc_gqa_attn_decode needs for this shape
+ * (max_len: the largest length it will be called with).  0 for an invalid
+ * shape.
+ */
+size_t rgc_gqa_attn_decode_workspace_size(int B, int Hq, int Hkv, int D,
+                                          int max_len);
+
+/*
+ * rgc_gqa_attn_decode -- one query row per sequence against its cache
+ * (cached generation).
+ *   o         [B,Hq,D] of dtype, strides (o_sb, o_sh); written.
+ *   q         [B,Hq,D] of dtype, strides (q_sb, q_sh); already rotated.
+ *   k_cache, v_cache  as in prefill.
+ *   seq_lens  [B] int32: cache length of sequence b INCLUDING the new
+ *             token, which sits at slot seq_lens[b] - 1 and is the query's
+ *             own position.
+ *   max_len   host: an upper bound of every seq_lens[b], 1..S_max; it sizes
+ *             the launch.  Pass S_max when unknown.
+ *   workspace device scratch of at least
+ *             rgc_gqa_attn_decode_workspace_size(B, Hq, Hkv, D, max_len)
+ *             bytes, 256-byte aligned.  Zero-fill it ONCE after allocating
+ *             it: the kernels keep per-(sequence, KV head) arrival counters
+ *             there and leave them at zero when a call completes.  Calls
+ *             that overlap in time must use different workspaces.
+ *   lse       [B,Hq] fp32 or NULL.
+ * Same arithmetic as prefill.  The cache is split along its length; the
+ * partial results are merged by max-rescaled sums.  A sequence with
+ * seq_lens outside [1, min(max_len, S_max)] gets NaN rows and a flag.
+ */
+int rgc_gqa_attn_decode(void* o, const void* q, const void* k_cache,
+                        const void* v_cache, int dtype, int B, int Hq, int Hkv,
+                        int D, int S_max, int64_t q_sb, int64_t q_sh,
+                        int64_t o_sb, int64_t o_sh, int64_t kv_sb,
+                        int64_t kv_sh, int64_t kv_ss, const int32_t* seq_lens,
+                        int max_len, float scale, void* workspace,
+                        size_t ws_bytes, float* lse, int32_t* err_flag,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGC_H */

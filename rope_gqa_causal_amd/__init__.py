@@ -1,0 +1,203 @@
+"""MI355X (gfx950) library for causal grouped-query attention with rotary
+position embedding over a key/value cache: prefill and cached decode.
+
+The compute runs in hand-written HIP kernels inside ``librgc.so`` (C ABI in
+``include/rgc.h``).  This module is a thin ctypes binding with the same
+names: it checks that tensors live on the GPU, passes their pointers,
+strides and torch's current stream, and turns a negative status into an
+exception.  It never computes anything itself and there is no fallback: if
+the library is missing or no GPU is present, every call raises.
+
+    import rope_gqa_causal_amd as rgc
+    rgc.rope_apply(q, pos0)                   # in place, q [B,S,Hq,D]
+    rgc.kv_cache_append(kc, vc, k, v, lens)   # caches [B,Hkv,S_max,D]
+    o = rgc.gqa_attn_prefill(q, kc, vc, q_start)
+    o = rgc.gqa_attn_decode(q1, kc, vc, lens, max_len, ws)
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RgcError", "library", "rope_apply", "kv_cache_append", "gqa_attn_prefill",
+    "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace",
+    "ROPE_HALF", "ROPE_INTERLEAVED",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librgc.so")
+ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+_F32, _BF16 = 0, 1
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_f = ctypes.c_float
+_d = ctypes.c_double
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "rgc_abi_version": (_i, []),
+    "rgc_status_string": (ctypes.c_char_p, [_i]),
+    "rgc_rope_apply": (_i, [_p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _d, _i, _p]),
+    "rgc_kv_cache_append": (_i, [_p, _p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _p, _i,
+                                 _i64, _i64, _i64, _p, _p, _p]),
+    "rgc_gqa_attn_prefill": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                  _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  _p, _f, _p, _p, _p]),
+    "rgc_gqa_attn_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "rgc_gqa_attn_decode": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                 _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                 _p, _i, _f, _p, _sz, _p, _p, _p]),
+}
+
+_lib = None
+
+
+class RgcError(RuntimeError):
+    """A negative status from the C ABI (nothing was launched)."""
+
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn}: status {status} ({text})")
+        self.status = status
+
+
+def library():
+    """Load ``librgc.so`` (built by ``rope_gqa_causal_amd.build``); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m rope_gqa_causal_amd.build` "
+                "(there is no CPU fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _call(name, *args):
+    lib = library()
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        raise RgcError(name, st, lib.rgc_status_string(st).decode())
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("rope_gqa_causal_amd works on GPU tensors only")
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _lens(t, B, name):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
+        raise ValueError(f"{name} must be a contiguous int32 tensor of {B} elements")
+    return t
+
+
+def rope_apply(x, pos0=None, base=10000.0, style=ROPE_HALF):
+    """Rotate x [B,S,H,D] in place; token (b,s) sits at position pos0[b] + s."""
+    _gpu(x, pos0)
+    B, S, H, D = x.shape
+    pos0 = _lens(pos0, B, "pos0")
+    _call("rgc_rope_apply", _ptr(x), _dtype(x), B, S, H, D, x.stride(0), x.stride(1),
+          x.stride(2), _ptr(pos0), float(base), int(style), _stream(x))
+    return x
+
+
+def kv_cache_append(k_cache, v_cache, k_new, v_new, pos0, err_flag=None):
+    """Copy k_new, v_new [B,S_new,Hkv,D] to slots pos0[b].. of caches [B,Hkv,S_max,D]."""
+    _gpu(k_cache, v_cache, k_new, v_new, pos0, err_flag)
+    B, Hkv, S_max, D = k_cache.shape
+    S_new = k_new.shape[1]
+    if v_cache.stride() != k_cache.stride() or v_new.stride() != k_new.stride():
+        raise ValueError("k and v tensors must share strides")
+    if tuple(k_new.shape) != (B, S_new, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("new rows must be [B,S_new,Hkv,D]")
+    pos0 = _lens(pos0, B, "pos0")
+    _call("rgc_kv_cache_append", _ptr(k_cache), _ptr(v_cache), _dtype(k_cache), B, Hkv, D, S_max,
+          k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), _ptr(k_new), _ptr(v_new),
+          S_new, k_new.stride(0), k_new.stride(1), k_new.stride(2), _ptr(pos0),
+          _ptr(err_flag), _stream(k_cache))
+
+
+def gqa_attn_prefill(q, k_cache, v_cache, q_start=None, scale=None, out=None, lse=None,
+                     err_flag=None):
+    """Causal GQA of q [B,Sq,Hq,D] over caches [B,Hkv,S_max,D] (row s at slot q_start[b]+s)."""
+    _gpu(q, k_cache, v_cache, q_start, out, lse, err_flag)
+    B, Sq, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    if v_cache.stride() != k_cache.stride():
+        raise ValueError("k_cache and v_cache must share strides")
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q) if out is None else out
+    q_start = _lens(q_start, B, "q_start")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq, Sq)):
+        raise ValueError("lse must be a contiguous float32 [B,Hq,Sq] tensor")
+    _call("rgc_gqa_attn_prefill", _ptr(o), _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype(q),
+          B, Sq, Hq, Hkv, D, S_max, q.stride(0), q.stride(1), q.stride(2),
+          o.stride(0), o.stride(1), o.stride(2),
+          k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+          _ptr(q_start), float(scale), _ptr(lse), _ptr(err_flag), _stream(q))
+    return o
+
+
+def gqa_attn_decode_workspace_size(B, Hq, Hkv, D, max_len):
+    return int(library().rgc_gqa_attn_decode_workspace_size(B, Hq, Hkv, D, max_len))
+
+
+def decode_workspace(B, Hq, Hkv, D, max_len, device="cuda"):
+    """A zero-filled workspace tensor large enough for gqa_attn_decode."""
+    n = max(gqa_attn_decode_workspace_size(B, Hq, Hkv, D, max_len), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def gqa_attn_decode(q, k_cache, v_cache, seq_lens, max_len=None, workspace=None, scale=None,
+                    out=None, lse=None, err_flag=None):
+    """One query row per sequence (q [B,Hq,D]) at slot seq_lens[b]-1 over its cache."""
+    _gpu(q, k_cache, v_cache, seq_lens, workspace, out, lse, err_flag)
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    if v_cache.stride() != k_cache.stride():
+        raise ValueError("k_cache and v_cache must share strides")
+    if scale is None:
+        scale = D ** -0.5
+    if max_len is None:
+        max_len = S_max
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, Hkv, D, max_len, q.device)
+    o = torch.empty_like(q) if out is None else out
+    seq_lens = _lens(seq_lens, B, "seq_lens")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq)):
+        raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
+    _call("rgc_gqa_attn_decode", _ptr(o), _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype(q),
+          B, Hq, Hkv, D, S_max, q.stride(0), q.stride(1), o.stride(0), o.stride(1),
+          k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), _ptr(seq_lens), int(max_len),
+          float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+          _ptr(lse), _ptr(err_flag), _stream(q))
+    return o

@@ -1,0 +1,63 @@
+// launch.h -- internal launch interface between the C ABI (api.hip) and the
+// kernels.  Every launcher enqueues on `stream` and returns the HIP status of
+// the launch; argument checking happens before, in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rgc {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { ROPE_HALF = 0, ROPE_INTERLEAVED = 1 };
+
+constexpr int kMaxRopeDim = 256;
+
+struct RopeParams {
+  void* x;
+  int B, S, H, D;
+  int64_t sb, ss, sh;
+  const int32_t* pos0;
+  double theta[kMaxRopeDim / 2];  // base^(-2i/D), formed on the host in fp64
+};
+hipError_t launch_rope(const RopeParams& p, int dtype, int style, hipStream_t stream);
+
+struct AppendParams {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;
+  const void* v_new;
+  int B, Hkv, D, S_max, S_new;
+  int64_t c_sb, c_sh, c_ss;
+  int64_t sb, ss, sh;
+  const int32_t* pos0;
+  int32_t* err;
+};
+hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t stream);
+
+// Causal attention over a cache.  Query row s of sequence b sits at slot
+// q_start[b] + s (prefill), or at seq_lens[b] - 1 with Sq == 1 (decode).
+struct AttnParams {
+  void* o;
+  const void* q;
+  const void* k;
+  const void* v;
+  int B, Sq, Hq, Hkv, D, S_max;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t kv_sb, kv_sh, kv_ss;
+  const int32_t* q_start;   // prefill
+  const int32_t* seq_lens;  // decode
+  int max_len;              // decode: host bound on seq_lens
+  float scale;
+  float* lse;               // [B,Hq,Sq] or NULL
+  int32_t* err;
+};
+hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams& p, bool decode, hipStream_t stream);
+
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len);
+hipError_t launch_decode_bf16(const AttnParams& p, void* ws, hipStream_t stream);
+
+}  // namespace rgc

@@ -1,0 +1,125 @@
+"""The C ABI library loads, exports what include/rgc.h declares, and checks
+its arguments on the host before any HIP call (no GPU needed: every call here
+is rejected or is a no-op before a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rope_gqa_causal_amd as rgc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rgc.h")
+
+# Status codes from include/rgc.h
+OK, NULL, SHAPE, GROUP, DTYPE, HEADDIM, LAYOUT, CAPACITY, WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+BF16, F32 = 1, 0
+A = 0x10000  # a 16-byte-aligned fake device address; never dereferenced by a rejected call
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(rgc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported():
+    lib = rgc.library()
+    names = _declared()
+    assert {"rgc_rope_apply", "rgc_kv_cache_append", "rgc_gqa_attn_prefill",
+            "rgc_gqa_attn_decode", "rgc_gqa_attn_decode_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    lib = rgc.library()
+    assert lib.rgc_abi_version() == 1
+    for st in range(-10, 1):
+        assert lib.rgc_status_string(st)
+    assert lib.rgc_status_string(GROUP).decode() == "Hq is not a multiple of Hkv"
+
+
+def _prefill(**kw):
+    a = dict(o=A, q=A, k=A, v=A, dt=BF16, B=1, Sq=4, Hq=4, Hkv=2, D=128, S_max=16,
+             q_sb=4 * 4 * 128, q_ss=4 * 128, q_sh=128, o_sb=4 * 4 * 128, o_ss=4 * 128, o_sh=128,
+             kv_sb=2 * 16 * 128, kv_sh=16 * 128, kv_ss=128, q_start=None, scale=0.1, lse=None, err=None)
+    a.update(kw)
+    return rgc.library().rgc_gqa_attn_prefill(
+        a["o"], a["q"], a["k"], a["v"], a["dt"], a["B"], a["Sq"], a["Hq"], a["Hkv"], a["D"], a["S_max"],
+        a["q_sb"], a["q_ss"], a["q_sh"], a["o_sb"], a["o_ss"], a["o_sh"], a["kv_sb"], a["kv_sh"],
+        a["kv_ss"], a["q_start"], a["scale"], a["lse"], a["err"], None)
+
+
+def test_prefill_rejects_bad_arguments_before_launch():
+    assert _prefill(Hq=3, Hkv=2) == GROUP          # configuration assertion: Hq % Hkv
+    assert _prefill(dt=7) == DTYPE
+    assert _prefill(D=96) == HEADDIM
+    assert _prefill(Sq=-1) == SHAPE
+    assert _prefill(Hkv=0) == SHAPE
+    assert _prefill(q=None) == NULL
+    assert _prefill(o=A + 2) == LAYOUT
+    assert _prefill(q_ss=4 * 128 + 1) == LAYOUT
+    assert _prefill(Sq=17) == CAPACITY
+    assert _prefill(scale=float("nan")) == -10
+    assert _prefill(B=0) == OK                      # empty batch: a no-op
+    assert _prefill(Sq=0) == OK
+
+
+def _decode(**kw):
+    a = dict(o=A, q=A, k=A, v=A, dt=BF16, B=2, Hq=4, Hkv=2, D=64, S_max=32, q_sb=256, q_sh=64,
+             o_sb=256, o_sh=64, kv_sb=2 * 32 * 64, kv_sh=32 * 64, kv_ss=64, lens=A, max_len=32,
+             scale=0.125, ws=A, ws_bytes=1 << 20, lse=None, err=None)
+    a.update(kw)
+    return rgc.library().rgc_gqa_attn_decode(
+        a["o"], a["q"], a["k"], a["v"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["D"], a["S_max"],
+        a["q_sb"], a["q_sh"], a["o_sb"], a["o_sh"], a["kv_sb"], a["kv_sh"], a["kv_ss"], a["lens"],
+        a["max_len"], a["scale"], a["ws"], a["ws_bytes"], a["lse"], a["err"], None)
+
+
+def test_decode_rejects_bad_arguments_before_launch():
+    assert _decode(Hq=6, Hkv=4) == GROUP
+    assert _decode(lens=None) == NULL
+    assert _decode(max_len=33) == CAPACITY
+    assert _decode(max_len=0) == CAPACITY
+    assert _decode(ws=None) == WORKSPACE
+    assert _decode(ws_bytes=16) == WORKSPACE
+    assert _decode(ws=A + 16) == LAYOUT
+    assert _decode(kv_ss=68) == LAYOUT
+    assert _decode(D=48) == HEADDIM
+    assert _decode(B=0) == OK
+
+
+def test_decode_workspace_size_grows_with_the_split_count():
+    lib = rgc.library()
+    one = lib.rgc_gqa_attn_decode_workspace_size(64, 24, 8, 128, 256)
+    many = lib.rgc_gqa_attn_decode_workspace_size(64, 24, 8, 128, 2080)
+    assert 0 < one < many
+    assert lib.rgc_gqa_attn_decode_workspace_size(64, 24, 8, 100, 2080) == 0
+
+
+def test_rope_and_append_reject_bad_arguments_before_launch():
+    lib = rgc.library()
+    rope = lambda **kw: lib.rgc_rope_apply(kw.get("x", A), kw.get("dt", BF16), 1, 4, 2, kw.get("D", 64),
+                                           512, 128, 64, None, kw.get("base", 10000.0),
+                                           kw.get("style", 0), None)
+    assert rope(D=3) == HEADDIM
+    assert rope(D=258) == HEADDIM
+    assert rope(style=2) == -10
+    assert rope(base=-1.0) == -10
+    assert rope(x=None) == NULL
+    assert rope(x=A + 1) == LAYOUT
+    app = lambda **kw: lib.rgc_kv_cache_append(A, A, BF16, 1, 2, kw.get("D", 64), kw.get("S_max", 8),
+                                               1024, 512, 64, A, A, kw.get("S_new", 4), 512, 128, 64,
+                                               kw.get("pos0", A), None, None)
+    assert app(S_new=9) == CAPACITY
+    assert app(pos0=None) == NULL
+    assert app(D=40) == HEADDIM
+    assert app(S_new=0) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rgc.rope_apply(x)

@@ -1,0 +1,86 @@
+"""GPU parity: RoPE and cache append against the fp64 oracle."""
+import pytest
+import torch
+
+import oracle
+import rope_gqa_causal_amd as rgc
+from rope_gqa_causal_amd import synth
+from _util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("style", [rgc.ROPE_HALF, rgc.ROPE_INTERLEAVED])
+@pytest.mark.parametrize("D", [2, 6, 32, 64, 128])
+def test_rope_fp32(style, D):
+    B, S, H = 3, 37, 5
+    x = synth.normal((B, S, H, D), synth.generator(D + style), torch.float32)
+    pos0 = torch.tensor([0, 4093, 123457], dtype=torch.int32)
+    ref = oracle.rope_f64(x, pos0, 10000.0, style)
+    y = x.cuda()
+    rgc.rope_apply(y, pos0.cuda(), 10000.0, style)
+    assert_close(y, ref, torch.float32, f"rope fp32 D={D} style={style}")
+
+
+@pytest.mark.parametrize("style", [rgc.ROPE_HALF, rgc.ROPE_INTERLEAVED])
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_bf16(style, D):
+    B, S, H = 2, 129, 8
+    x = synth.normal((B, S, H, D), synth.generator(100 + D), torch.bfloat16)
+    pos0 = torch.tensor([0, 1919], dtype=torch.int32)
+    exact = oracle.rope_f64(x, pos0, 10000.0, style)
+    once = oracle.rope_apply_(x.clone(), pos0, 10000.0, style)
+    y = x.cuda()
+    rgc.rope_apply(y, pos0.cuda(), 10000.0, style)
+    assert_close(y, exact, torch.bfloat16, "rope bf16")
+    # The GPU rounds an fp32 result once; it may differ from the single
+    # rounding of the exact value only where fp32 error straddles a tie.
+    same = (y.cpu().view(torch.int16) == once.view(torch.int16)).float().mean().item()
+    assert same > 0.99
+
+
+def test_rope_strided_heads_and_no_position_array():
+    # q as a view into a packed [B,S,3,H,D] qkv buffer; pos0 = NULL means 0.
+    B, S, H, D = 2, 16, 4, 64
+    qkv = synth.normal((B, S, 3, H, D), synth.generator(7), torch.bfloat16)
+    q = qkv[:, :, 0]
+    ref = oracle.rope_f64(q, None, 10000.0, rgc.ROPE_HALF)
+    g = qkv.cuda()
+    rgc.rope_apply(g[:, :, 0], None)
+    assert_close(g[:, :, 0], ref, torch.bfloat16, "strided rope")
+    assert torch.equal(g[:, :, 1:].cpu(), qkv[:, :, 1:])  # k and v untouched
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_append_bit_exact(dtype, D):
+    B, Hkv, S_max, S_new = 4, 3, 40, 7
+    g = synth.generator(D)
+    kc, vc = synth.nan_cache(B, Hkv, S_max, D, dtype)
+    k_new = synth.normal((B, S_new, Hkv, D), g, dtype)
+    v_new = synth.normal((B, S_new, Hkv, D), g, dtype)
+    pos0 = torch.tensor([0, 5, 33, 17], dtype=torch.int32)
+    kref, vref = kc.clone(), vc.clone()
+    assert oracle.kv_cache_append_(kref, vref, k_new, v_new, pos0) == 0
+    kg, vg = kc.cuda(), vc.cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rgc.kv_cache_append(kg, vg, k_new.cuda(), v_new.cuda(), pos0.cuda(), err)
+    ibits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(kg.cpu().view(ibits), kref.view(ibits))
+    assert torch.equal(vg.cpu().view(ibits), vref.view(ibits))
+    assert err.item() == 0
+
+
+def test_append_out_of_capacity_is_flagged_and_skipped():
+    B, Hkv, S_max, D, S_new = 2, 2, 16, 64, 4
+    g = synth.generator(3)
+    kc, vc = synth.nan_cache(B, Hkv, S_max, D)
+    k_new = synth.normal((B, S_new, Hkv, D), g)
+    pos0 = torch.tensor([2, 14], dtype=torch.int32)   # second sequence overflows by 2
+    kref, vref = kc.clone(), vc.clone()
+    oracle.kv_cache_append_(kref, vref, k_new, k_new, pos0)
+    kg, vg = kc.cuda(), vc.cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rgc.kv_cache_append(kg, vg, k_new.cuda(), k_new.cuda(), pos0.cuda(), err)
+    assert err.item() == 1
+    assert torch.equal(kg.cpu().view(torch.int16), kref.view(torch.int16))
