@@ -8,27 +8,29 @@
 //
 // HBM-bound (about 3 flop per cache byte).  Design:
 //  * split-K over the cache length: a workgroup owns one (sequence, KV head,
-//    head subgroup) and a 256-key chunk, so a ragged batch spreads over many
-//    workgroups of equal size; empty chunks of short sequences exit at once;
+//    head subgroup) and a chunk of 128 keys (256 at head dim 32), so a
+//    ragged batch spreads over many workgroups of equal size; empty chunks of
+//    short sequences exit at once;
 //  * every K and V byte of the chunk is read exactly once, with 16-byte
 //    loads that cover whole rows, and serves all the query heads of the
 //    group (up to 4 per workgroup);
-//  * all of a wave's loads are issued before any arithmetic, so each wave
-//    keeps 32 KB of the cache in flight;
+//  * all of a wave's loads are issued before any arithmetic;
 //  * q.k uses packed bf16 dot products (v_dot2_f32_bf16) over a 4-lane key
 //    layout that needs only two quad swizzles per key; the probabilities go
 //    through LDS to a second layout in which each lane accumulates 8 output
-//    elements of 16 keys, so p.V needs no per-key reduction;
-//  * a chunk's partial (max, sum, unnormalised output) is written to the
-//    workspace and a second kernel merges the chunks by max-rescaled sums.
-//    A sequence that fits in one chunk is finished by the first kernel.
+//    elements of its keys, so p.V needs no per-key reduction;
+//  * a chunk's partial (max, sum, unnormalised output) goes to the
+//    workspace and a second, small kernel merges the chunks by max-rescaled
+//    sums.  A sequence that fits in one chunk is finished by the first.
+//    (Merging inside the first kernel, by the last chunk to arrive, would
+//    need device-scope fences, and on gfx950 each of those writes back and
+//    invalidates the XCD's L2: measured 16x slower than the second launch.)
 #include "common.h"
 #include "launch.h"
 
 namespace rgc {
 namespace {
 
-constexpr int kChunk = 256;  // keys per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -73,9 +75,18 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// Keys per wave and per workgroup (4 waves).  A wave covers at least one
+// pass of the q.k layout (64 / (D / 32) keys).
+template <int D>
+struct Chunk {
+  static constexpr int WAVE_KEYS = (64 / (D / 32)) > 32 ? (64 / (D / 32)) : 32;
+  static constexpr int KEYS = 4 * WAVE_KEYS;
+};
+int chunk_keys(int D) { return D == 32 ? Chunk<32>::KEYS : D == 64 ? Chunk<64>::KEYS : Chunk<128>::KEYS; }
+
 struct DecodeWs {
-  float* part_o;   // [B][Hq][NS][D]  unnormalised partial outputs
-  float* part_ml;  // [B][Hq][NS][2]  (max in log2 units, sum)
+  float* part_o;    // [B][Hq][NS][D]  unnormalised partial outputs
+  float* part_ml;   // [B][Hq][NS][2]  (max in log2 units, sum)
   int NS;
 };
 
@@ -87,14 +98,15 @@ __device__ __forceinline__ bool len_ok(const AttnParams& p, int L) {
 // D: head dim; GS: query heads per workgroup (all of them share KV head kvh).
 template <int D, int GS>
 __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeWs ws, int nsub) {
+  constexpr int WK = Chunk<D>::WAVE_KEYS;
   constexpr int LPK = D / 32;      // lanes per key in the q.k layout
   constexpr int KPP = 64 / LPK;    // keys per pass
-  constexpr int PASSES = LPK;      // passes over the wave's 64 keys
+  constexpr int PASSES = WK / KPP; // passes over the wave's keys
   constexpr int LPR = D / 8;       // lanes per row in the p.V layout
   constexpr int KPI = 64 / LPR;    // keys per load in the p.V layout
-  constexpr int VLOADS = 64 / KPI; // = LPR
+  constexpr int VLOADS = WK / KPI;
 
-  __shared__ f32x4 p_lds[4][64];
+  __shared__ f32x4 p_lds[4][WK];
   __shared__ float o_lds[4][GS][D];
   __shared__ float ml_lds[4][GS][2];
 
@@ -118,13 +130,13 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
     }
     return;
   }
-  const int k0 = split * kChunk;
+  const int k0 = split * Chunk<D>::KEYS;
   if (k0 >= L) return;
-  const int ns = (L + kChunk - 1) / kChunk;
+  const int ns = (L + Chunk<D>::KEYS - 1) / Chunk<D>::KEYS;
 
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int kw = k0 + wave * 64;
+  const int kw = k0 + wave * WK;
   const float c = p.scale * kLog2e;
 
   const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
@@ -143,7 +155,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
   const int part = lane % LPK, key_sub = lane / LPK;
   const int dgrp = lane % LPR, kq = lane / LPR;
   if (active) {
-    // ---- issue every load of the wave's 64 keys ----
+    // ---- issue every load of the wave's keys ----
     u32x4 kf[PASSES][4], vf[VLOADS];
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
@@ -258,7 +270,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
     if (ns == 1) {
       bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
       orow[d] = f32_to_bf16(o / lsum);
-      if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = (M + __log2f(lsum)) * kLn2;
+      if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = (M + log2f(lsum)) * kLn2;
     } else {
       const int64_t slot = ((int64_t)b * p.Hq + h) * ws.NS + split;
       ws.part_o[slot * D + d] = o;
@@ -276,20 +288,20 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, DecodeW
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int L = p.seq_lens[b];
   if (!len_ok(p, L)) return;
-  const int ns = (L + kChunk - 1) / kChunk;
+  const int ns = (L + Chunk<D>::KEYS - 1) / Chunk<D>::KEYS;
   if (ns <= 1) return;
   const int64_t base = ((int64_t)b * p.Hq + h) * ws.NS;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ws.part_ml[(base + s) * 2]);
+  for (int c = 0; c < ns; ++c) M = fmaxf(M, ws.part_ml[(base + c) * 2]);
   float lsum = 0.f, o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float f = exp2f(ws.part_ml[(base + s) * 2] - M);
-    lsum = fmaf(ws.part_ml[(base + s) * 2 + 1], f, lsum);
-    o = fmaf(ws.part_o[(base + s) * D + d], f, o);
+  for (int c = 0; c < ns; ++c) {
+    const float f = exp2f(ws.part_ml[(base + c) * 2] - M);
+    lsum = fmaf(ws.part_ml[(base + c) * 2 + 1], f, lsum);
+    o = fmaf(ws.part_o[(base + c) * D + d], f, o);
   }
   bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
   orow[d] = f32_to_bf16(o / lsum);
-  if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = (M + __log2f(lsum)) * kLn2;
+  if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = (M + log2f(lsum)) * kLn2;
 }
 
 int heads_per_wg(int group) {
@@ -318,21 +330,33 @@ hipError_t launch_d(const AttnParams& p, DecodeWs ws, hipStream_t stream) {
 
 }  // namespace
 
+// Workspace: partial outputs, then partial (max, sum) pairs.
+struct WsLayout {
+  int NS;
+  size_t o_bytes, ml_bytes;
+};
+WsLayout ws_layout(int B, int Hq, int D, int max_len) {
+  WsLayout l;
+  const int chunk = chunk_keys(D);
+  l.NS = (max_len + chunk - 1) / chunk;
+  const int64_t slots = (int64_t)B * Hq * l.NS;
+  l.o_bytes = ((size_t)(slots * D * 4) + 255) & ~(size_t)255;
+  l.ml_bytes = ((size_t)(slots * 2 * 4) + 255) & ~(size_t)255;
+  return l;
+}
+
 size_t decode_workspace_bytes(int B, int Hq, int /*Hkv*/, int D, int max_len) {
-  const int64_t ns = (max_len + kChunk - 1) / kChunk;
-  const int64_t slots = (int64_t)B * Hq * ns;
-  size_t o_bytes = (size_t)(slots * D * 4);
-  o_bytes = (o_bytes + 255) & ~(size_t)255;
-  return o_bytes + (size_t)(slots * 2 * 4);
+  const WsLayout l = ws_layout(B, Hq, D, max_len);
+  return l.o_bytes + l.ml_bytes;
 }
 
 hipError_t launch_decode_bf16(const AttnParams& p, void* workspace, hipStream_t stream) {
+  const WsLayout l = ws_layout(p.B, p.Hq, p.D, p.max_len);
   DecodeWs ws;
-  ws.NS = (p.max_len + kChunk - 1) / kChunk;
-  const int64_t slots = (int64_t)p.B * p.Hq * ws.NS;
-  size_t o_bytes = ((size_t)(slots * p.D * 4) + 255) & ~(size_t)255;
-  ws.part_o = reinterpret_cast<float*>(workspace);
-  ws.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+  ws.NS = l.NS;
+  char* base = reinterpret_cast<char*>(workspace);
+  ws.part_o = reinterpret_cast<float*>(base);
+  ws.part_ml = reinterpret_cast<float*>(base + l.o_bytes);
   switch (p.D) {
     case 32: return launch_d<32>(p, ws, stream);
     case 64: return launch_d<64>(p, ws, stream);

@@ -6,24 +6,33 @@
 // and 无效的方法; the m.nxbn.cn build-an-LLM page, section 3.1): row s of
 // sequence b at slot p attends to slots 0..p of its KV head.
 //
-// A dense contraction (QK^T then PV), so it runs on bf16 MFMA
+// A dense contraction (QK^T then PV) on bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//  * a workgroup owns one (sequence, KV head, head subgroup) and 128 query
-//    positions; each of its 4 waves owns 32 positions of every head in the
-//    subgroup (NB heads), so one K/V tile staged in LDS feeds all of them;
+//  * a workgroup of 8 waves owns one query head and 256 query positions;
+//    each wave owns 32 positions.  Two waves share a SIMD (<= 256 registers
+//    each), so one wave's softmax (VALU) runs under the other's MFMAs;
 //  * scores are computed transposed, S^T = K Q^T (keys in the MFMA M
-//    dimension), which leaves each lane holding one query's column: the
-//    online-softmax max and sum are in-lane except one swap with the lane
-//    32 away, and the probabilities are already laid out as the B operand of
-//    O^T = V^T P^T, so P never leaves registers;
-//  * K tiles sit in LDS row-major with a 16-byte XOR swizzle (conflict-free
-//    row reads); V tiles are transposed while being staged (two keys per
-//    32-bit LDS word) so that V^T fragments are two 8-byte LDS reads;
-//  * the next K/V tile is fetched from HBM into registers while the current
-//    one is multiplied (LDS double buffer, one barrier per tile);
-//  * tiles above the causal diagonal are skipped per wave, and workgroups
-//    are issued heaviest q-tile first; the blockIdx -> (KV head, tile)
-//    mapping keeps every tile of one KV head on one XCD (shared L2).
+//    dimension): a lane holds one query's column, so the softmax max and sum
+//    are in-lane except one v_permlane32_swap with the lane 32 away, and the
+//    probabilities are already in the B-operand layout of O^T = V^T P^T --
+//    P never leaves registers;
+//  * 64-key K and V tiles are staged HBM -> registers -> LDS through a
+//    3-slot ring (tile j read, j+1 ready, j+2 written), one barrier per tile;
+//    the global loads of tile j+2 are in flight while tile j is multiplied;
+//  * both tiles stay row-major in LDS with a per-row XOR swizzle of their
+//    16-byte chunks: K fragments (A operand of S^T) are conflict-free 16-byte
+//    reads, and V^T fragments (A operand of O^T) come straight from the
+//    row-major V tile through ds_read_b64_tr_b16, the gfx950 transposing LDS
+//    read -- V is never transposed in software;
+//  * the loop is unrolled over the ring so every LDS address is a per-lane
+//    base register plus an immediate offset, and tile loads use a scalar base
+//    plus a per-lane 32-bit offset: the VALU does softmax work only.  The
+//    causal mask is applied on diagonal tiles only;
+//  * the running max is only raised (and O rescaled) when a tile's max
+//    exceeds it by more than 2^8, so the rescale is almost never taken; p is
+//    then at most 256, exact in fp32 and within bf16 range;
+//  * tiles above a wave's causal diagonal are skipped, workgroups are
+//    issued heaviest q-tile first.
 #include "common.h"
 #include "launch.h"
 
@@ -32,301 +41,379 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kWaves = 4;
-constexpr int kBM = 32 * kWaves;  // query positions per workgroup
-constexpr int kKT = 32;           // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;   // query positions per workgroup
+constexpr int kKT = 64;            // keys per tile
+constexpr int kSlots = 3;          // LDS ring: tile j read, j+1 ready, j+2 written
+constexpr int kXcds = 8;           // MI355X: workgroup i is dispatched to XCD i % 8
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
 
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// max / sum of x[lane] and x[lane ^ 32] with one v_permlane32_swap: the swap
+// hands each half the other half's value in one of its two results.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS layout: kSlots K tiles, then kSlots V tiles, each row-major
+// [64 keys][D] in 16-byte chunks; chunk c of row r sits at chunk c ^ swz(r).
+//  K: swz = r % CH, so the 16 rows of one K-fragment read hit 16 chunks.
+//  V: swz = 4 * tv(r), an XOR of the 32-row d-block index by tv(r) (the low
+//     bits of r that vary inside a transposed read), which spreads the 4
+//     rows x 4 chunks of a half-wave read over all 64 banks.
 template <int D>
 struct Tile {
-  static constexpr int CH = D / 8;                 // 16-byte chunks per row
-  static constexpr int K_UNITS = kKT * CH;         // chunks in a K tile
-  static constexpr int V_UNITS = (kKT / 2) * CH;   // (key pair, chunk) units
-  static constexpr int K_PER_T = (K_UNITS + 255) / 256;
-  static constexpr int V_PER_T = (V_UNITS + 255) / 256;
-  static constexpr int VT_STRIDE = kKT + 4;        // bf16 per V^T row (72 B)
-  static constexpr int K_ELEMS = kKT * D;
-  static constexpr int VT_ELEMS = D * VT_STRIDE;
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int KS = D / 16;                  // k-steps of QK^T
+  static constexpr int DB = D / 32;                  // 32-row blocks of O^T
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int MAT_BYTES = kKT * ROW_BYTES;  // one K or V tile
+  static constexpr int V_REGION = kSlots * MAT_BYTES;
+  static constexpr int LDS_BYTES = 2 * kSlots * MAT_BYTES;
+  static constexpr int PIECES = MAT_BYTES / 1024;    // 1 KB pieces per tile
+  static constexpr int LOADS = 2 * PIECES / kWaves;  // 16-byte pieces per lane per tile
+  static __device__ __forceinline__ int swz_k(int r) { return r % CH; }
+  static __device__ __forceinline__ constexpr int tv(int r) {
+    return D == 128 ? (r & 3) : D == 64 ? ((r >> 1) & 1) : 0;
+  }
+  // The lane's piece i: matrix (0 = K, 1 = V), row and logical chunk.
+  static __device__ __forceinline__ void piece(int wave, int lane, int i, int& mat, int& r, int& c, int& P) {
+    const int g = wave * LOADS + i;
+    mat = g / PIECES;
+    P = (g % PIECES) * 64 + lane;
+    r = P / CH;
+    const int pc = P % CH;
+    c = pc ^ (mat == 0 ? swz_k(r) : 4 * tv(r));
+  }
+};
+
+// Tile staging: wave w's i-th piece covers 1 KB of a slot contiguously (lane
+// l at byte 16l); the lane fetches the logical chunk stored there.
+template <int D>
+struct Stager {
+  uint32_t goff[Tile<D>::LOADS];   // byte offset in HBM from the tile's first row
+  uint32_t loff[Tile<D>::LOADS];   // byte offset in LDS of the piece in slot 0
 };
 
 template <int D>
-struct Stage {
-  u32x4 k[Tile<D>::K_PER_T];
-  u32x4 v[Tile<D>::V_PER_T][2];
-};
-
-// Fetch tile [j0, j0+32) of K and V into registers; keys past kmax read as 0
-// (never from memory), so no unwritten cache slot can reach the arithmetic.
-template <int D>
-__device__ __forceinline__ void fetch_tile(Stage<D>& st, const bf16_t* kb, const bf16_t* vb,
-                                           int64_t kv_ss, int j0, int kmax, int tid) {
+__device__ __forceinline__ void make_stager(Stager<D>& sg, int64_t kv_ss, int wave, int lane) {
   using T = Tile<D>;
 #pragma unroll
-  for (int i = 0; i < T::K_PER_T; ++i) {
-    const int u = tid + 256 * i;
-    st.k[i] = u32x4{0, 0, 0, 0};
-    if (u < T::K_UNITS) {
-      const int key = j0 + u / T::CH, c = u % T::CH;
-      if (key <= kmax) st.k[i] = ld16(kb + (int64_t)key * kv_ss + 8 * c);
-    }
+  for (int i = 0; i < T::LOADS; ++i) {
+    int mat, r, c, P;
+    T::piece(wave, lane, i, mat, r, c, P);
+    sg.goff[i] = (uint32_t)(r * kv_ss * 2 + 16 * c);
+    sg.loff[i] = (mat ? T::V_REGION : 0) + 16 * P;
   }
+}
+
+// HBM -> registers for tile [j0, j0+64).  Rows past kmax (only in a
+// workgroup's last tile) are clamped to kmax: their keys are masked and their
+// probabilities are 0, so the clamped (finite, written) rows never reach a
+// result and no unwritten cache slot is read.
+template <int D>
+__device__ __forceinline__ void fetch_tile(u32x4 (&st)[Tile<D>::LOADS], const Stager<D>& sg, const char* kb,
+                                           const char* vb, int64_t kv_ss, int j0, int kmax, int wave,
+                                           int lane) {
+  using T = Tile<D>;
+  if (j0 + kKT - 1 <= kmax) {
+    const char* kt = kb + (int64_t)j0 * kv_ss * 2;
+    const char* vt = vb + (int64_t)j0 * kv_ss * 2;
 #pragma unroll
-  for (int i = 0; i < T::V_PER_T; ++i) {
-    const int u = tid + 256 * i;
-    st.v[i][0] = st.v[i][1] = u32x4{0, 0, 0, 0};
-    if (u < T::V_UNITS) {
-      const int key = j0 + 2 * (u / T::CH), c = u % T::CH;
-      if (key <= kmax) st.v[i][0] = ld16(vb + (int64_t)key * kv_ss + 8 * c);
-      if (key + 1 <= kmax) st.v[i][1] = ld16(vb + (int64_t)(key + 1) * kv_ss + 8 * c);
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int mat = (wave * T::LOADS + i) / T::PIECES;
+      st[i] = ld16((mat ? vt : kt) + sg.goff[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      int mat, r, c, P;
+      T::piece(wave, lane, i, mat, r, c, P);
+      const int key = min(j0 + r, kmax);
+      st[i] = ld16((mat ? vb : kb) + (int64_t)key * kv_ss * 2 + 16 * c);
     }
   }
 }
 
-// Registers -> LDS: K row-major with chunk c of key r at chunk (c ^ (r % CH));
-// V transposed, element (d, key) at vt[d * VT_STRIDE + key].
-template <int D>
-__device__ __forceinline__ void store_tile(const Stage<D>& st, bf16_t* ks, bf16_t* vt, int tid) {
+template <int D, int SLOT>
+__device__ __forceinline__ void store_tile(const u32x4 (&st)[Tile<D>::LOADS], const Stager<D>& sg, char* lds) {
   using T = Tile<D>;
 #pragma unroll
-  for (int i = 0; i < T::K_PER_T; ++i) {
-    const int u = tid + 256 * i;
-    if (u < T::K_UNITS) {
-      const int r = u / T::CH, c = u % T::CH;
-      *reinterpret_cast<u32x4*>(ks + r * D + 8 * (c ^ (r % T::CH))) = st.k[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < T::V_PER_T; ++i) {
-    const int u = tid + 256 * i;
-    if (u < T::V_UNITS) {
-      const int kp = u / T::CH, c = u % T::CH;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t a = st.v[i][0][e], bb = st.v[i][1][e];
-        // (d = 8c+2e): keys (2kp, 2kp+1) -> low halves; (d = 8c+2e+1): high halves
-        const uint32_t lo = (a & 0xFFFFu) | (bb << 16);
-        const uint32_t hi = (a >> 16) | (bb & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e) * T::VT_STRIDE + 2 * kp) = lo;
-        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * e + 1) * T::VT_STRIDE + 2 * kp) = hi;
-      }
-    }
-  }
+  for (int i = 0; i < T::LOADS; ++i)
+    *reinterpret_cast<u32x4*>(lds + sg.loff[i] + SLOT * T::MAT_BYTES) = st[i];
 }
 
-// D: head dim (64 or 128); NB: query heads per wave (the head subgroup).
-template <int D, int NB>
-__global__ void __launch_bounds__(256, 1) prefill_kernel(AttnParams p, int nsub, int nqt) {
-  using T = Tile<D>;
-  constexpr int KS = D / 16;   // k-steps of QK^T
-  constexpr int DB = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) bf16_t k_lds[2][T::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2][T::VT_ELEMS];
+// V^T fragment: two transposed 8-byte reads.  In each 16-lane group (h =
+// lane/32 picks the key half, (lane/16)%2 the 16-row half of the d block)
+// lane x supplies the address of 4 consecutive d of key 16kk + 4h + x/4 (+8
+// for the second read); lane j then holds those 4 keys' values at
+// d = 32db + lane%32 -- the MFMA A-operand layout.
+template <int D>
+__device__ __forceinline__ u32x4 vt_frag(const char* a) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * Tile<D>::ROW_BYTES));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
 
-  const int nunits = p.B * p.Hkv * nsub;
-  const int unit = blockIdx.x % nunits;
-  const int qt = nqt - 1 - (int)(blockIdx.x / nunits);  // heaviest tiles first
-  const int hs = unit % nsub;
-  const int kvh = (unit / nsub) % p.Hkv;
-  const int b = unit / (nsub * p.Hkv);
+template <int D>
+struct WaveCtx {
+  u32x4 qf[D / 16];          // Q^T fragments (B operand)
+  const char* kp[D / 16];    // K-fragment address in slot 0, per k-step
+  const char* vp[D / 32];    // V^T-fragment address in slot 0, per d-block
+  f32x16 acc_o[D / 32];
+  float m_run, l_run;
+  float c;                   // scale * log2(e)
+  int mask_base;             // qabs - 4*half: key offset limit is mask_base - j0
+};
+
+// Scores, online softmax and O update for the tile in slot SLOT.
+template <int D, int SLOT, bool MASK>
+__device__ __forceinline__ void compute_tile(WaveCtx<D>& w, int j0) {
+  using T = Tile<D>;
+  constexpr int KS = T::KS, DB = T::DB;
+  // ---- S^T = K Q^T: block kb holds keys 32kb + 8(r/4) + 4half + r%4 ----
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    u32x4 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = *reinterpret_cast<const u32x4*>(w.kp[ks] + SLOT * T::MAT_BYTES + kb * 32 * T::ROW_BYTES);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s[kb] = mfma(kf[ks], w.qf[ks], s[kb]);
+  }
+  // ---- causal mask (diagonal tiles only) ----
+  if (MASK) {
+    const int lim = w.mask_base - j0;  // keep key offsets <= lim
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+  }
+  // ---- online softmax (log2 domain) ----
+  float m0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+  float m1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) {
+    m0 = fmaxf(fmaxf(m0, s[0][r]), s[0][r + 1]);
+    m1 = fmaxf(fmaxf(m1, s[1][r]), s[1][r + 1]);
+  }
+  m0 = fmaxf(fmaxf(m0, s[0][15]), m1);
+  m0 = fmaxf(m0, s[1][15]);
+  const float tmax = max_halves(m0) * w.c;
+  // Raise the running max only when the tile's max exceeds it by more than
+  // the threshold (wave-uniform decision).
+  const bool need = tmax > w.m_run + kRescaleThreshold;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    asm volatile("; rescale" ::);  // keeps this rare path a real branch (no if-conversion)
+    const float m_new = need ? tmax : w.m_run;
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);  // 0 on the first tile
+    w.m_run = m_new;
+    w.l_run *= alpha;
+#pragma unroll
+    for (int q = 0; q < DB; ++q)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.acc_o[q][r] *= alpha;
+  }
+  // p = 2^(s*c - m), rounded to bf16 for the PV product; the row sum adds
+  // the same rounded values (packed bf16 dot products with 1.0), so the
+  // numerator and the denominator use identical weights.
+  u32x4 pf[4];
+  float ps0 = 0.f, ps1 = 0.f;
+  constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1.0, 1.0)
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e], w.c, -w.m_run));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e + 1], w.c, -w.m_run));
+      pf[kk][e] = pack_bf16x2(p0, p1);
+      if (e & 1) ps1 = dot2_bf16(pf[kk][e], kOnes, ps1);
+      else ps0 = dot2_bf16(pf[kk][e], kOnes, ps0);
+    }
+  }
+  w.l_run += ps0 + ps1;
+  // ---- O^T += V^T P^T ----
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int q = 0; q < DB; ++q)
+      w.acc_o[q] = mfma(vt_frag<D>(w.vp[q] + SLOT * T::MAT_BYTES + kk * 16 * T::ROW_BYTES), pf[kk], w.acc_o[q]);
+}
+
+// One step of the ring for tile jt in slot SLOT: fetch tile jt+2, multiply
+// tile jt, store tile jt+2 into the slot tile jt-1 used, barrier.
+template <int D, int SLOT>
+__device__ __forceinline__ void ring_step(WaveCtx<D>& w, u32x4 (&st)[Tile<D>::LOADS], const Stager<D>& sg,
+                                          char* lds, const char* kb, const char* vb, int64_t kv_ss, int jt,
+                                          int nkt, int kmax, int wave_last, int diag_from, int wave, int lane) {
+  const bool refill = jt + 2 < nkt;
+  if (refill) fetch_tile<D>(st, sg, kb, vb, kv_ss, (jt + 2) * kKT, kmax, wave, lane);
+  if (jt <= wave_last) {
+    if (jt < diag_from) compute_tile<D, SLOT, false>(w, jt * kKT);
+    else compute_tile<D, SLOT, true>(w, jt * kKT);
+  }
+  if (refill) store_tile<D, (SLOT + 2) % kSlots>(st, sg, lds);
+  __syncthreads();
+}
+
+// D: head dim (32, 64 or 128).
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int nqt) {
+  using T = Tile<D>;
+  constexpr int KS = T::KS, DB = T::DB;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+
+  // XCD-aware order.  Workgroup i runs on XCD i % 8; relabel so that each
+  // XCD walks a contiguous range of (sequence, KV head) groups, and within a
+  // group all its query heads and q-tiles, heaviest q-tile first.  The
+  // workgroups resident on one XCD then share one or two groups' K/V in
+  // that XCD's L2.
   const int group = p.Hq / p.Hkv;
-  const int h0 = kvh * group + hs * NB;
+  const int per_group = group * nqt;
+  const int total = p.B * p.Hkv * per_group;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int lid = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (lid >= total) return;
+  const int gidx = lid / per_group;      // (b, kvh)
+  const int widx = lid % per_group;
+  const int qt = nqt - 1 - widx / group;  // heaviest tiles first
+  const int kvh = gidx % p.Hkv;
+  const int b = gidx / p.Hkv;
+  const int h = kvh * group + widx % group;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
 
   const int first = p.q_start ? p.q_start[b] : 0;
   const int s_base = qt * kBM + wave * 32;  // this wave's first row
   if (first < 0 || (int64_t)first + p.Sq > p.S_max) {
-    // Device-side capacity violation: NaN rows, flag, no memory access.
+    // Device-side capacity violation: NaN rows, flag, no cache access.
     if (s_base + col < p.Sq && half == 0) {
-      for (int g = 0; g < NB; ++g) {
-        bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb +
-                       (int64_t)(s_base + col) * p.o_ss + (int64_t)(h0 + g) * p.o_sh;
-        for (int d = 0; d < D; ++d) orow[d] = 0x7FC0;
-        if (p.lse) p.lse[((int64_t)b * p.Hq + h0 + g) * p.Sq + s_base + col] = __builtin_nanf("");
-      }
+      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb +
+                     (int64_t)(s_base + col) * p.o_ss + (int64_t)h * p.o_sh;
+      for (int d = 0; d < D; ++d) orow[d] = 0x7FC0;
+      if (p.lse) p.lse[((int64_t)b * p.Hq + h) * p.Sq + s_base + col] = __builtin_nanf("");
     }
     if (tid == 0 && p.err) p.err[0] = 1;
     return;
   }
 
-  const int s_end_wg = min(p.Sq, (qt + 1) * kBM);           // rows [qt*kBM, s_end_wg)
-  const int kmax = first + s_end_wg - 1;                      // last key the workgroup needs
+  const int s_end_wg = min(p.Sq, (qt + 1) * kBM);     // rows [qt*kBM, s_end_wg)
+  const int kmax = first + s_end_wg - 1;                // last key the workgroup needs
   const int nkt = kmax / kKT + 1;
-  const int wave_rows = min(32, p.Sq - s_base);               // may be <= 0 (ragged tail)
-  const int wave_kmax = first + s_base + wave_rows - 1;       // last key this wave needs
-  const float c = p.scale * kLog2e;
+  const int wave_rows = min(32, p.Sq - s_base);         // <= 0: a wave past the ragged tail
+  const int wave_last = wave_rows > 0 ? (first + s_base + wave_rows - 1) / kKT : -1;
+  const int diag_from = (first + s_base) / kKT;         // first tile that needs the mask
 
-  const bf16_t* kb = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
-  const bf16_t* vb = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
+  const char* kb = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh) * 2;
+  const char* vb = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh) * 2;
 
-  // Q^T fragments (B operand): lane holds query `col`, d = 16*ks + 8*half .. +8.
-  u32x4 qf[NB][KS];
+  WaveCtx<D> w;
+  w.c = p.scale * kLog2e;
+  w.mask_base = first + s_base + col - 4 * half;
   {
+    // Q^T fragments: lane holds query `col`, d = 16*ks + 8*half .. +8.
     const int s = s_base + col;
+    const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb +
+                       (int64_t)s * p.q_ss + (int64_t)h * p.q_sh;
 #pragma unroll
-    for (int g = 0; g < NB; ++g) {
-      const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb +
-                         (int64_t)s * p.q_ss + (int64_t)(h0 + g) * p.q_sh;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[g][ks] = (s < p.Sq) ? ld16(qr + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      w.qf[ks] = (s < p.Sq) ? ld16(qr + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
   }
-
-  f32x16 acc_o[NB][DB];
-  float m_run[NB], l_run[NB];
+  // K fragment: row `col` (block 1 is 32 rows further) at logical chunk
+  // 2ks + half.  V^T fragment for d-block q: rows 4half + x/4 (+16kk, +8),
+  // logical chunk 4q + c_lane stored at physical chunk 4(q ^ tv(row)) +
+  // c_lane, 8-byte half x & 1.
 #pragma unroll
-  for (int g = 0; g < NB; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
+  for (int ks = 0; ks < KS; ++ks) w.kp[ks] = lds + col * T::ROW_BYTES + 16 * ((2 * ks + half) ^ T::swz_k(col));
+  {
+    const int x = lane & 15, beta = lane >> 4;
+    const int c_lane = 2 * (beta & 1) + ((x & 3) >> 1);
+    const int r0 = 4 * half + (x >> 2);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[g][db][r] = 0.f;
+    for (int q = 0; q < DB; ++q)
+      w.vp[q] = lds + T::V_REGION + r0 * T::ROW_BYTES + 16 * (4 * (q ^ T::tv(r0)) + c_lane) + 8 * (x & 1);
   }
+#pragma unroll
+  for (int q = 0; q < DB; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.acc_o[q][r] = 0.f;
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
 
-  Stage<D> st;
-  fetch_tile<D>(st, kb, vb, p.kv_ss, 0, kmax, tid);
-  store_tile<D>(st, k_lds[0], vt_lds[0], tid);
+  Stager<D> sg;
+  make_stager<D>(sg, p.kv_ss, wave, lane);
+
+  // Prologue: tiles 0 and 1 into slots 0 and 1.
+  u32x4 st[T::LOADS];
+  fetch_tile<D>(st, sg, kb, vb, p.kv_ss, 0, kmax, wave, lane);
+  store_tile<D, 0>(st, sg, lds);
+  if (nkt > 1) {
+    fetch_tile<D>(st, sg, kb, vb, p.kv_ss, kKT, kmax, wave, lane);
+    store_tile<D, 1>(st, sg, lds);
+  }
   __syncthreads();
 
-  const int qabs = first + s_base + col;  // this lane's query slot
-  for (int jt = 0; jt < nkt; ++jt) {
-    const int buf = jt & 1;
-    const bool more = jt + 1 < nkt;
-    if (more) fetch_tile<D>(st, kb, vb, p.kv_ss, (jt + 1) * kKT, kmax, tid);
-
-    const int j0 = jt * kKT;
-    if (wave_rows > 0 && j0 <= wave_kmax) {
-      const bf16_t* ks_ = k_lds[buf];
-      const bf16_t* vt_ = vt_lds[buf];
-      // ---- S^T = K Q^T: lane gets keys 8*(r/4) + 4*half + r%4 of query col ----
-      f32x16 sacc[NB];
-#pragma unroll
-      for (int g = 0; g < NB; ++g)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[g][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int cidx = 2 * ks + half;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(ks_ + col * D + 8 * (cidx ^ (col % T::CH)));
-#pragma unroll
-        for (int g = 0; g < NB; ++g) sacc[g] = mfma(a, qf[g][ks], sacc[g]);
-      }
-      // ---- online softmax (log2 domain) ----
-      const bool diag = j0 + kKT - 1 > first + s_base;
-      u32x4 pf[NB][2];
-#pragma unroll
-      for (int g = 0; g < NB; ++g) {
-        if (diag) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key > qabs) sacc[g][r] = -INFINITY;
-          }
-        }
-        float tmax = sacc[g][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[g][r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run[g], tmax * c);
-        const float alpha = exp2f(m_run[g] - m_new);
-        m_run[g] = m_new;
-        float psum = 0.f;
-        float pr[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pr[r] = exp2f(fmaf(sacc[g][r], c, -m_new));
-          psum += pr[r];
-        }
-        l_run[g] = fmaf(l_run[g], alpha, psum);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[g][db][r] *= alpha;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pf[g][kk][e] = pack_bf16x2(pr[8 * kk + 2 * e], pr[8 * kk + 2 * e + 1]);
-      }
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16_t* vrow = vt_ + (32 * db + col) * T::VT_STRIDE + 16 * kk + 4 * half;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int g = 0; g < NB; ++g) acc_o[g][db] = mfma(a, pf[g][kk], acc_o[g][db]);
-        }
-      }
-    }
-    if (more) store_tile<D>(st, k_lds[buf ^ 1], vt_lds[buf ^ 1], tid);
-    __syncthreads();
+  for (int jt = 0; jt < nkt; jt += kSlots) {
+    ring_step<D, 0>(w, st, sg, lds, kb, vb, p.kv_ss, jt, nkt, kmax, wave_last, diag_from, wave, lane);
+    if (jt + 1 >= nkt) break;
+    ring_step<D, 1>(w, st, sg, lds, kb, vb, p.kv_ss, jt + 1, nkt, kmax, wave_last, diag_from, wave, lane);
+    if (jt + 2 >= nkt) break;
+    ring_step<D, 2>(w, st, sg, lds, kb, vb, p.kv_ss, jt + 2, nkt, kmax, wave_last, diag_from, wave, lane);
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16 ----
-  const int s = s_base + col;
-  if (wave_rows > 0 && s < p.Sq) {
-#pragma unroll
-    for (int g = 0; g < NB; ++g) {
-      const float lsum = l_run[g] + __shfl_xor(l_run[g], 32, 64);
+  // acc_o[q] register r holds d = 32q + 8(r/4) + 4half + r%4 of query col.
+  if (wave_last >= 0) {
+    const float lsum = sum_halves(w.l_run);
+    const int s = s_base + col;
+    if (s < p.Sq) {
       const float inv = 1.f / lsum;
       bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)s * p.o_ss +
-                     (int64_t)(h0 + g) * p.o_sh;
+                     (int64_t)h * p.o_sh;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int q = 0; q < DB; ++q)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = 32 * db + 8 * q4 + 4 * half;
-          u32x2 w;
-          w[0] = pack_bf16x2(acc_o[g][db][4 * q4] * inv, acc_o[g][db][4 * q4 + 1] * inv);
-          w[1] = pack_bf16x2(acc_o[g][db][4 * q4 + 2] * inv, acc_o[g][db][4 * q4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d) = w;
+          const int d = 32 * q + 8 * q4 + 4 * half;
+          u32x2 wv;
+          wv[0] = pack_bf16x2(w.acc_o[q][4 * q4] * inv, w.acc_o[q][4 * q4 + 1] * inv);
+          wv[1] = pack_bf16x2(w.acc_o[q][4 * q4 + 2] * inv, w.acc_o[q][4 * q4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d) = wv;
         }
-      if (p.lse && half == 0) p.lse[((int64_t)b * p.Hq + h0 + g) * p.Sq + s] = (m_run[g] + log2f(lsum)) * kLn2;
+      if (p.lse && half == 0)
+        p.lse[((int64_t)b * p.Hq + h) * p.Sq + s] = (w.m_run + log2f(lsum)) * kLn2;
     }
   }
-}
-
-// Query heads per wave: as many of the group as the register file holds
-// without spilling (the O^T and Q^T fragments grow with NB * D).
-int heads_per_wave(int group, int D) {
-  const int cap = D == 128 ? 2 : 4;
-  for (int nb = cap; nb >= 1; --nb)
-    if (group % nb == 0) return nb;
-  return 1;
-}
-
-template <int D, int NB>
-void launch_nb(const AttnParams& p, int nsub, int nqt, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.B * p.Hkv * nsub * nqt));
-  hipLaunchKernelGGL((prefill_kernel<D, NB>), grid, dim3(256), 0, stream, p, nsub, nqt);
 }
 
 template <int D>
 hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
-  const int group = p.Hq / p.Hkv;
-  const int nb = heads_per_wave(group, D);
-  const int nsub = group / nb;
   const int nqt = (p.Sq + kBM - 1) / kBM;
-  if (D == 128) {
-    if (nb == 2) launch_nb<D, 2>(p, nsub, nqt, stream);
-    else launch_nb<D, 1>(p, nsub, nqt, stream);
-  } else {
-    switch (nb) {
-      case 4: launch_nb<D, (D == 128 ? 1 : 4)>(p, nsub, nqt, stream); break;
-      case 3: launch_nb<D, (D == 128 ? 1 : 3)>(p, nsub, nqt, stream); break;
-      case 2: launch_nb<D, 2>(p, nsub, nqt, stream); break;
-      default: launch_nb<D, 1>(p, nsub, nqt, stream); break;
-    }
-  }
+  const int total = p.B * p.Hq * nqt;
+  const dim3 grid((unsigned)(((total + kXcds - 1) / kXcds) * kXcds));
+  hipLaunchKernelGGL(prefill_kernel<D>, grid, dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream, p, nqt);
   return hipGetLastError();
 }
 

@@ -3,6 +3,8 @@
 Inputs are seeded normal draws; every cache slot the call must not read holds
 a NaN canary, so a read past a length shows up as a NaN in the result.
 """
+import math
+
 import pytest
 import torch
 
@@ -12,6 +14,8 @@ from rope_gqa_causal_amd import synth
 from _util import assert_close
 
 pytestmark = pytest.mark.gpu
+
+LSE_TOL_BF16 = math.log1p(2.0 ** -9) + 1e-4
 
 
 def _prefill_case(B, Sq, Hq, Hkv, D, dtype, q_start, S_max, seed):
@@ -47,7 +51,10 @@ def test_prefill_bf16(case):
     o = rgc.gqa_attn_prefill(q.cuda(), kc.cuda(), vc.cuda(), qs.cuda(), lse=lse)
     torch.cuda.synchronize()
     assert_close(o, ref, torch.bfloat16, "prefill bf16")
-    assert (lse.cpu().double() - ref_lse).abs().max().item() < 1e-3
+    # The bf16 kernels normalise by the sum of the bf16-rounded weights they
+    # multiply V with; each weight carries a relative error <= 2^-9, so the
+    # sum, and exp(lse), is off by at most that: |d lse| <= log(1 + 2^-9).
+    assert (lse.cpu().double() - ref_lse).abs().max().item() < LSE_TOL_BF16
 
 
 @pytest.mark.parametrize("case", [(1, 16, 4, 2, 32, [0], 24), (2, 70, 6, 3, 64, [0, 5], 80),
