@@ -2,10 +2,12 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
   prefill phase  (24 query / 8 KV heads, head dim 128, batch 8 x 2048 tokens):
-                 RoPE on q and k, cache append, causal GQA prefill;
+                 fused RoPE on q and k + cache append, causal GQA prefill;
   decode phase   (64 sequences, cache lengths uniform on {256..2048}, same
-                 heads): 32 generation steps of RoPE on the new q and k,
-                 cache append, length update and cached GQA decode.
+                 heads): 32 generation steps of fused RoPE on the new q and
+                 k + cache append, then cached GQA decode (the lengths of
+                 every step are precomputed once, as a serving loop knows
+                 them).
 `value` is the decode phase's KV-read rate (cache bytes every decode call
 must read / decode-phase time, GB/s); the prefill phase's attention rate is
 reported beside it (TFLOP/s over unmasked query-key pairs).  Both are also
@@ -81,9 +83,8 @@ class Prefill:
 
     def run(self, record):
         r = self.rgc
-        r.rope_apply(self.q, self.pos0)
-        r.rope_apply(self.k, self.pos0)
-        r.kv_cache_append(self.kc, self.vc, self.k, self.v, self.pos0)
+        # RoPE on q and k and the cache append in one fused pass.
+        r.rope_append(self.q, self.k, self.v, self.kc, self.vc, self.pos0)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -107,8 +108,11 @@ class Decode:
         self.q = q.view(w.steps, w.B, 1, w.Hq, w.D).cuda()
         self.k = k.view(w.steps, w.B, 1, w.Hkv, w.D).cuda()
         self.v = v.view(w.steps, w.B, 1, w.Hkv, w.D).cuda()
-        self.lens0 = self.lens0_cpu.cuda()
-        self.lens = self.lens0.clone()
+        # Lengths of every step, computed once: step t appends at slot
+        # lens0 + t and then attends over lens0 + t + 1 rows.
+        steps = torch.arange(w.steps, dtype=torch.int32)[:, None]
+        self.slots = (self.lens0_cpu[None, :] + steps).contiguous().cuda()
+        self.lens = (self.lens0_cpu[None, :] + steps + 1).contiguous().cuda()
         self.o = torch.empty((w.B, w.Hq, w.D), dtype=w.dtype, device="cuda")
         self.ws = rgc.decode_workspace(w.B, w.Hq, w.Hkv, w.D, self.S_max)
         self.rgc = rgc
@@ -120,16 +124,13 @@ class Decode:
 
     def run(self, record):
         r, w = self.rgc, self.w
-        self.lens.copy_(self.lens0)
         for t in range(w.steps):
-            r.rope_apply(self.q[t], self.lens)
-            r.rope_apply(self.k[t], self.lens)
-            r.kv_cache_append(self.kc, self.vc, self.k[t], self.v[t], self.lens)
-            self.lens += 1
+            # fused RoPE (q, k at position lens0 + t) and cache append
+            r.rope_append(self.q[t], self.k[t], self.v[t], self.kc, self.vc, self.slots[t])
             if record:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-            r.gqa_attn_decode(self.q[t][:, 0], self.kc, self.vc, self.lens, self.S_max, self.ws,
+            r.gqa_attn_decode(self.q[t][:, 0], self.kc, self.vc, self.lens[t], self.S_max, self.ws,
                               out=self.o)
             if record:
                 e1.record()
@@ -243,7 +244,7 @@ def main():
         "prefill": {
             "tflops": round(prefill_tflops, 2),
             "phase_ms_per_step": round(pre_ms / args.steps, 4),
-            "note": "RoPE q,k + append + causal prefill; FLOPs count unmasked pairs x 4D",
+            "note": "fused RoPE q,k + append, then causal prefill; FLOPs count unmasked pairs x 4D",
         },
         "decode_phase_ms_per_step": round(dec_ms / args.steps, 4),
         "roofline": {

@@ -122,6 +122,31 @@ int rgc_kv_cache_append(void* k_cache, void* v_cache, int dtype, int B,
                         const int32_t* pos0, int32_t* err_flag, void* stream);
 
 /*
+ * rgc_rope_append -- the fused prologue of a generation step: RoPE on the
+ * new tokens' q and k and the append of k and v to the caches, in one pass
+ * over the data (the first page's section V3 describes the step: the new
+ * token computes its q, k, v, which are rotated at its position, and its k
+ * and v join the cache).
+ *   q              [B,S,Hq,D] of dtype, strides (q_sb, q_ss, q_sh); rotated
+ *                  in place.
+ *   k_new, v_new   [B,S,Hkv,D] of dtype, strides (sb, ss, sh) shared by
+ *                  both; read only.
+ *   k_cache, v_cache  [B,Hkv,S_max,D] of dtype, strides (c_sb, c_sh, c_ss).
+ *   pos0           [B] int32: token (b, s) has position and cache slot
+ *                  pos0[b] + s.
+ * Equivalent to rgc_rope_apply on q and on a copy of k_new, followed by
+ * rgc_kv_cache_append of the rotated k and of v_new, bit for bit; k_new
+ * itself is left unrotated.  A token whose slot falls outside [0, S_max)
+ * still has its q rotated; its k and v are skipped and flagged.  Head dim
+ * 32, 64 or 128; pointers and strides 16-byte aligned.
+ */
+int rgc_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, int dtype,
+                    int B, int S, int Hq, int Hkv, int D, int S_max, int64_t q_sb, int64_t q_ss,
+                    int64_t q_sh, int64_t sb, int64_t ss, int64_t sh, int64_t c_sb, int64_t c_sh,
+                    int64_t c_ss, const int32_t* pos0, double base, int style, int32_t* err_flag,
+                    void* stream);
+
+/*
  * rgc_gqa_attn_prefill -- causal GQA attention of a block of query rows over
  * the cache.
  *   o        [B,Sq,Hq,D] of dtype, strides (o_sb, o_ss, o_sh); written.
@@ -170,10 +195,11 @@ size_t rgc_gqa_attn_decode_workspace_size(int B, int Hq, int Hkv, int D,
  *             the launch.  Pass S_max when unknown.
  *   workspace device scratch of at least
  *             rgc_gqa_attn_decode_workspace_size(B, Hq, Hkv, D, max_len)
- *             bytes, 256-byte aligned.  Zero-fill it ONCE after allocating
- *             it: the kernels keep per-(sequence, KV head) arrival counters
- *             there and leave them at zero when a call completes.  Calls
- *             that overlap in time must use different workspaces.
+ *             bytes, 256-byte aligned, owned by the caller.  It holds the
+ *             per-chunk partial results of one call; its contents need no
+ *             initialisation and are meaningless afterwards.  Calls that
+ *             overlap in time must use different workspaces.  With an
+ *             fp32 dtype the workspace is not used (may be NULL).
  *   lse       [B,Hq] fp32 or NULL.
  * Same arithmetic as prefill.  The cache is split along its length; the
  * partial results are merged by max-rescaled sums.  A sequence with

@@ -110,6 +110,52 @@ int rgc_kv_cache_append(void* k_cache, void* v_cache, int dtype, int B, int Hkv,
   return hip_status(launch_append(p, dtype, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int rgc_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, int dtype,
+                    int B, int S, int Hq, int Hkv, int D, int S_max, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                    int64_t sb, int64_t ss, int64_t sh, int64_t c_sb, int64_t c_sh, int64_t c_ss,
+                    const int32_t* pos0, double base, int style, int32_t* err_flag, void* stream) {
+  if (!dtype_ok(dtype)) return RGC_ERR_DTYPE;
+  if (B < 0 || S < 0 || Hq < 0 || Hkv < 0 || D < 0 || S_max < 0) return RGC_ERR_SHAPE;
+  if (!headdim_ok(D)) return RGC_ERR_HEADDIM;
+  if (style != RGC_ROPE_HALF && style != RGC_ROPE_INTERLEAVED) return RGC_ERR_ARG;
+  if (!(base > 0.0) || !std::isfinite(base)) return RGC_ERR_ARG;
+  if (B == 0 || S == 0 || (Hq == 0 && Hkv == 0)) return RGC_OK;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !pos0) return RGC_ERR_NULL;
+  if (S > S_max) return RGC_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return RGC_ERR_LAYOUT;
+  if (!stride_ok(q_sb, dtype) || !stride_ok(q_ss, dtype) || !stride_ok(q_sh, dtype) || !stride_ok(sb, dtype) ||
+      !stride_ok(ss, dtype) || !stride_ok(sh, dtype) || !stride_ok(c_sb, dtype) || !stride_ok(c_sh, dtype) ||
+      !stride_ok(c_ss, dtype))
+    return RGC_ERR_LAYOUT;
+  RopeAppendParams p;
+  p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.B = B;
+  p.S = S;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.S_max = S_max;
+  p.q_sb = q_sb;
+  p.q_ss = q_ss;
+  p.q_sh = q_sh;
+  p.n_sb = sb;
+  p.n_ss = ss;
+  p.n_sh = sh;
+  p.c_sb = c_sb;
+  p.c_sh = c_sh;
+  p.c_ss = c_ss;
+  p.pos0 = pos0;
+  p.err = err_flag;
+  for (int i = 0; i < kMaxRopeDim / 2; ++i)
+    p.theta[i] = i < D / 2 ? std::pow(base, -2.0 * (double)i / (double)D) : 0.0;
+  return hip_status(launch_rope_append(p, dtype, style, reinterpret_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 int check_attn_common(int dtype, int B, int Sq, int Hq, int Hkv, int D, int S_max) {

@@ -23,6 +23,24 @@ struct RopeParams {
 };
 hipError_t launch_rope(const RopeParams& p, int dtype, int style, hipStream_t stream);
 
+// Fused prologue: RoPE on q (in place) and on the new k, then k and v into
+// the caches; the token's position is its cache slot pos0[b] + s.
+struct RopeAppendParams {
+  void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  int B, S, Hq, Hkv, D, S_max;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t n_sb, n_ss, n_sh;
+  int64_t c_sb, c_sh, c_ss;
+  const int32_t* pos0;
+  int32_t* err;
+  double theta[kMaxRopeDim / 2];
+};
+hipError_t launch_rope_append(const RopeAppendParams& p, int dtype, int style, hipStream_t stream);
+
 struct AppendParams {
   void* k_cache;
   void* v_cache;

@@ -84,3 +84,50 @@ def test_append_out_of_capacity_is_flagged_and_skipped():
     rgc.kv_cache_append(kg, vg, k_new.cuda(), k_new.cuda(), pos0.cuda(), err)
     assert err.item() == 1
     assert torch.equal(kg.cpu().view(torch.int16), kref.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("style", [rgc.ROPE_HALF, rgc.ROPE_INTERLEAVED])
+@pytest.mark.parametrize("S,D", [(1, 128), (37, 64), (5, 32)])
+def test_rope_append_equals_rope_then_append_bit_for_bit(dtype, style, S, D):
+    B, Hq, Hkv, S_max = 3, 6, 2, 64
+    g = synth.generator(S * D + style)
+    q, k, v = synth.qkv(B, S, Hq, Hkv, D, g, dtype)
+    pos0 = torch.tensor([0, 9, S_max - S], dtype=torch.int32).cuda()
+    # separate calls
+    q1, k1 = q.cuda(), k.cuda().clone()
+    kc1, vc1 = [t.cuda() for t in synth.nan_cache(B, Hkv, S_max, D, dtype)]
+    rgc.rope_apply(q1, pos0, 10000.0, style)
+    rgc.rope_apply(k1, pos0, 10000.0, style)
+    rgc.kv_cache_append(kc1, vc1, k1, v.cuda(), pos0)
+    # fused
+    q2, k2 = q.cuda(), k.cuda()
+    kc2, vc2 = [t.cuda() for t in synth.nan_cache(B, Hkv, S_max, D, dtype)]
+    rgc.rope_append(q2, k2, v.cuda(), kc2, vc2, pos0, 10000.0, style)
+    ibits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(q1.cpu().view(ibits), q2.cpu().view(ibits))
+    assert torch.equal(kc1.cpu().view(ibits), kc2.cpu().view(ibits))
+    assert torch.equal(vc1.cpu().view(ibits), vc2.cpu().view(ibits))
+    assert torch.equal(k2.cpu().view(ibits), k.view(ibits))  # k_new itself is not rotated
+
+
+def test_rope_append_matches_the_oracle_and_flags_capacity():
+    B, S, Hq, Hkv, D, S_max = 2, 4, 12, 4, 64, 40
+    g = synth.generator(77)
+    q, k, v = synth.qkv(B, S, Hq, Hkv, D, g)
+    pos0 = torch.tensor([3, 38], dtype=torch.int32)   # second sequence runs 2 slots past the end
+    ref_q = oracle.rope_f64(q, pos0)
+    ref_k = oracle.rope_apply_(k.clone(), pos0)
+    kc_ref, vc_ref = synth.nan_cache(B, Hkv, S_max, D)
+    oracle.kv_cache_append_(kc_ref, vc_ref, ref_k, v, pos0)
+    qg = q.cuda()
+    kc, vc = [t.cuda() for t in synth.nan_cache(B, Hkv, S_max, D)]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rgc.rope_append(qg, k.cuda(), v.cuda(), kc, vc, pos0.cuda(), err_flag=err)
+    assert err.item() == 1
+    assert_close(qg, ref_q, torch.bfloat16, "fused rope q")
+    assert torch.equal(vc.cpu().view(torch.int16), vc_ref.view(torch.int16))
+    got, want = kc.cpu(), kc_ref
+    written = ~torch.isnan(want)
+    assert torch.equal(torch.isnan(got), torch.isnan(want))          # same slots written
+    assert (got[written].double() - want[written].double()).abs().max().item() <= 2 ** -7 * 4
