@@ -7,18 +7,26 @@
 // sequence, the query heads of a group sharing one KV head.
 //
 // HBM-bound (about 3 flop per cache byte).  Design:
-//  * split-K over the cache length: a workgroup owns one (sequence, KV head,
-//    head subgroup) and a chunk of 128 keys (256 at head dim 32), so a
-//    ragged batch spreads over many workgroups of equal size; empty chunks of
-//    short sequences exit at once;
+//  * split-K over the cache length: a workgroup of four waves owns one
+//    (sequence, KV head, head subgroup) and a chunk of 4 x 64 keys (4 x 32
+//    when the batch is too small to fill the chip that way), so a ragged
+//    batch spreads over many workgroups of equal size; empty chunks of short
+//    sequences exit at once;
 //  * every K and V byte of the chunk is read exactly once, with 16-byte
-//    loads that cover whole rows, and serves all the query heads of the
-//    group (up to 4 per workgroup);
-//  * all of a wave's loads are issued before any arithmetic;
+//    loads, and serves all the query heads of the group (up to 4 per
+//    workgroup);
+//  * every load of a wave is unconditional and issued before any
+//    arithmetic: keys past the end re-read the last row and are masked in
+//    the scores.  (A guarded load per key makes the compiler wait for all
+//    earlier loads at each guard, which serialises the wave's memory
+//    traffic.)
 //  * q.k uses packed bf16 dot products (v_dot2_f32_bf16) over a 4-lane key
 //    layout that needs only two quad swizzles per key; the probabilities go
 //    through LDS to a second layout in which each lane accumulates 8 output
-//    elements of its keys, so p.V needs no per-key reduction;
+//    elements of its keys; there two keys' values of one element are paired
+//    by a byte permute and meet their two probabilities (rounded to bf16) in
+//    one packed dot product.  The key lanes are summed in the LDS merge of
+//    the four waves;
 //  * a chunk's partial (max, sum, unnormalised output) goes to the
 //    workspace and a second, small kernel merges the chunks by max-rescaled
 //    sums.  A sequence that fits in one chunk is finished by the first.
@@ -76,18 +84,23 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 // Keys per wave and per workgroup (4 waves).  A wave covers at least one
-// pass of the q.k layout (64 / (D / 32) keys).
-template <int D>
+// pass of the q.k layout (64 / (D / 32) keys), times MUL.
+constexpr int kWaves = 4;
+template <int D, int MUL>
 struct Chunk {
-  static constexpr int WAVE_KEYS = (64 / (D / 32)) > 32 ? (64 / (D / 32)) : 32;
-  static constexpr int KEYS = 4 * WAVE_KEYS;
+  static constexpr int WAVE_KEYS = ((64 / (D / 32)) > 32 ? (64 / (D / 32)) : 32) * MUL;
+  static constexpr int KEYS = kWaves * WAVE_KEYS;
 };
-int chunk_keys(int D) { return D == 32 ? Chunk<32>::KEYS : D == 64 ? Chunk<64>::KEYS : Chunk<128>::KEYS; }
+int chunk_keys(int D, int mul) {
+  const int wave_keys = (D == 32 ? 64 : 32) * mul;
+  return kWaves * wave_keys;
+}
 
 struct DecodeWs {
   float* part_o;    // [B][Hq][NS][D]  unnormalised partial outputs
   float* part_ml;   // [B][Hq][NS][2]  (max in log2 units, sum)
-  int NS;
+  int NS;           // chunks of the longest sequence
+  int chunk;        // keys per chunk
 };
 
 __device__ __forceinline__ bool len_ok(const AttnParams& p, int L) {
@@ -95,10 +108,11 @@ __device__ __forceinline__ bool len_ok(const AttnParams& p, int L) {
   return L >= 1 && L <= lim;
 }
 
-// D: head dim; GS: query heads per workgroup (all of them share KV head kvh).
-template <int D, int GS>
-__global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeWs ws, int nsub) {
-  constexpr int WK = Chunk<D>::WAVE_KEYS;
+// D: head dim; GS: query heads per workgroup (all of them share KV head kvh);
+// MUL: keys per wave in units of one q.k pass.
+template <int D, int GS, int MUL>
+__global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p, DecodeWs ws, int nsub) {
+  constexpr int WK = Chunk<D, MUL>::WAVE_KEYS;
   constexpr int LPK = D / 32;      // lanes per key in the q.k layout
   constexpr int KPP = 64 / LPK;    // keys per pass
   constexpr int PASSES = WK / KPP; // passes over the wave's keys
@@ -106,9 +120,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
   constexpr int KPI = 64 / LPR;    // keys per load in the p.V layout
   constexpr int VLOADS = WK / KPI;
 
-  __shared__ f32x4 p_lds[4][WK];
-  __shared__ float o_lds[4][GS][D];
-  __shared__ float ml_lds[4][GS][2];
+  __shared__ f32x4 p_lds[kWaves][WK];
+  __shared__ float o_lds[kWaves][KPI][GS][D];
+  __shared__ float ml_lds[kWaves][GS][2];
 
   const int split = blockIdx.x;
   const int hs = blockIdx.y % nsub;
@@ -121,7 +135,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
 
   if (!len_ok(p, L)) {
     if (split == 0) {
-      for (int i = tid; i < GS * D; i += 256) {
+      for (int i = tid; i < GS * D; i += 64 * kWaves) {
         bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)(h0 + i / D) * p.o_sh;
         orow[i % D] = 0x7FC0;  // NaN
       }
@@ -130,9 +144,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
     }
     return;
   }
-  const int k0 = split * Chunk<D>::KEYS;
+  const int k0 = split * Chunk<D, MUL>::KEYS;
   if (k0 >= L) return;
-  const int ns = (L + Chunk<D>::KEYS - 1) / Chunk<D>::KEYS;
+  const int ns = (L + Chunk<D, MUL>::KEYS - 1) / Chunk<D, MUL>::KEYS;
 
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -155,21 +169,10 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
   const int part = lane % LPK, key_sub = lane / LPK;
   const int dgrp = lane % LPR, kq = lane / LPR;
   if (active) {
-    // ---- issue every load of the wave's keys ----
-    u32x4 kf[PASSES][4], vf[VLOADS];
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int key = kw + ps * KPP + key_sub;
-      const bf16_t* kr = kbase + (int64_t)key * p.kv_ss;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        kf[ps][i] = key < L ? ld16(kr + 8 * (part + LPK * i)) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int t = 0; t < VLOADS; ++t) {
-      const int key = kw + t * KPI + kq;
-      vf[t] = key < L ? ld16(vbase + (int64_t)key * p.kv_ss + 8 * dgrp) : u32x4{0, 0, 0, 0};
-    }
+    // ---- issue every load of the wave's keys (q first: the scores need it
+    // before the values).  Keys past the end re-read the last row, which
+    // keeps every load unconditional and in bounds; their scores are masked
+    // to -inf, so they weigh nothing.
     u32x4 qf[GS][4];
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
@@ -177,6 +180,20 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
 #pragma unroll
       for (int i = 0; i < 4; ++i) qf[g][i] = ld16(qr + 8 * (part + LPK * i));
     }
+    u32x4 kf[PASSES][4], vf[VLOADS];
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int key = min(kw + ps * KPP + key_sub, L - 1);
+      const bf16_t* kr = kbase + (int64_t)key * p.kv_ss;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[ps][i] = ld16(kr + 8 * (part + LPK * i));
+    }
+#pragma unroll
+    for (int t = 0; t < VLOADS; ++t) {
+      const int key = min(kw + t * KPI + kq, L - 1);
+      vf[t] = ld16(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
 
     // ---- scores: z = scale * log2(e) * q.k ----
     float z[GS][PASSES];
@@ -220,31 +237,34 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes landed
     __builtin_amdgcn_wave_barrier();
-    // ---- p.V: lane owns d in [8*dgrp, 8*dgrp+8) for keys t*KPI + kq ----
+    // ---- p.V: lane owns d in [8*dgrp, 8*dgrp+8) for keys t*KPI + kq.
+    // Two keys at a time: their values of one d side by side in a bf16
+    // pair (one byte permute) meet the pair of their probabilities in one
+    // packed dot product.
 #pragma unroll
-    for (int t = 0; t < VLOADS; ++t) {
-      const f32x4 pv = p_lds[wave][t * KPI + kq];
+    for (int t = 0; t < VLOADS; t += 2) {
+      const f32x4 pa = p_lds[wave][t * KPI + kq];
+      const f32x4 pb = p_lds[wave][(t + 1) * KPI + kq];
+      uint32_t pp[GS];
+#pragma unroll
+      for (int g = 0; g < GS; ++g) pp[g] = pack_bf16x2(pa[g], pb[g]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v0 = bf16_lo(vf[t][e]), v1 = bf16_hi(vf[t][e]);
+        const uint32_t lo = __builtin_amdgcn_perm(vf[t + 1][e], vf[t][e], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(vf[t + 1][e], vf[t][e], 0x07060302u);
 #pragma unroll
         for (int g = 0; g < GS; ++g) {
-          acc[g][2 * e] = fmaf(pv[g], v0, acc[g][2 * e]);
-          acc[g][2 * e + 1] = fmaf(pv[g], v1, acc[g][2 * e + 1]);
+          acc[g][2 * e] = dot2(pp[g], lo, acc[g][2 * e]);
+          acc[g][2 * e + 1] = dot2(pp[g], hi, acc[g][2 * e + 1]);
         }
       }
     }
-#pragma unroll
-    for (int g = 0; g < GS; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] = sum_above<LPR>(acc[g][e]);
   }
-  // ---- merge the four waves ----
-  if (lane < LPR) {
+  // ---- merge the four waves and their KPI key lanes ----
 #pragma unroll
-    for (int g = 0; g < GS; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o_lds[wave][g][8 * lane + e] = acc[g][e];
+  for (int g = 0; g < GS; ++g) {
+    *reinterpret_cast<f32x4*>(&o_lds[wave][kq][g][8 * dgrp]) = f32x4{acc[g][0], acc[g][1], acc[g][2], acc[g][3]};
+    *reinterpret_cast<f32x4*>(&o_lds[wave][kq][g][8 * dgrp + 4]) = f32x4{acc[g][4], acc[g][5], acc[g][6], acc[g][7]};
   }
   if (lane == 0) {
 #pragma unroll
@@ -254,17 +274,20 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
     }
   }
   __syncthreads();
-  for (int i = tid; i < GS * D; i += 256) {
+  for (int i = tid; i < GS * D; i += 64 * kWaves) {
     const int g = i / D, d = i % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][g][0]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml_lds[w][g][0]);
     float lsum = 0.f, o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float f = exp2f(ml_lds[w][g][0] - M);  // 0 for a wave without keys
       lsum = fmaf(ml_lds[w][g][1], f, lsum);
-      o = fmaf(o_lds[w][g][d], f, o);
+      float ow = 0.f;
+#pragma unroll
+      for (int k = 0; k < KPI; ++k) ow += o_lds[w][k][g][d];
+      o = fmaf(ow, f, o);
     }
     const int h = h0 + g;
     if (ns == 1) {
@@ -284,24 +307,62 @@ __global__ void __launch_bounds__(256) decode_split_kernel(AttnParams p, DecodeW
 
 // Merge the chunks of one (sequence, query head): max-rescaled sums.
 template <int D>
-__global__ void __launch_bounds__(D) decode_combine_kernel(AttnParams p, DecodeWs ws) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__global__ void __launch_bounds__(256) decode_combine_kernel(AttnParams p, DecodeWs ws) {
+  // One wave per (sequence, query head).  The partial rows of the first
+  // kPre chunks and lane c's (max, sum) of chunk c are all loaded at once,
+  // so the merge waits for one round of loads; the global max and the
+  // rescaled sum are wave reductions, and each lane holds D / 64 outputs.
+  constexpr int EPL = D >= 64 ? D / 64 : 1;  // output elements per lane
+  constexpr int kPre = 16;
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= p.B * p.Hq) return;
+  const int b = bh / p.Hq, h = bh % p.Hq;
   const int L = p.seq_lens[b];
   if (!len_ok(p, L)) return;
-  const int ns = (L + Chunk<D>::KEYS - 1) / Chunk<D>::KEYS;
+  const int ns = (L + ws.chunk - 1) / ws.chunk;
   if (ns <= 1) return;
-  const int64_t base = ((int64_t)b * p.Hq + h) * ws.NS;
-  float M = -INFINITY;
-  for (int c = 0; c < ns; ++c) M = fmaxf(M, ws.part_ml[(base + c) * 2]);
-  float lsum = 0.f, o = 0.f;
-  for (int c = 0; c < ns; ++c) {
-    const float f = exp2f(ws.part_ml[(base + c) * 2] - M);
-    lsum = fmaf(ws.part_ml[(base + c) * 2 + 1], f, lsum);
-    o = fmaf(ws.part_o[(base + c) * D + d], f, o);
+  const int64_t base = (int64_t)bh * ws.NS;  // slot (b, h, c) = (b * Hq + h) * NS + c
+  const bool act = lane * EPL < D;
+  float v[kPre][EPL];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      v[u][e] = (act && u < ns) ? ws.part_o[(base + u) * D + lane * EPL + e] : 0.f;
+  const float m0 = lane < ns ? ws.part_ml[(base + lane) * 2] : -INFINITY;
+  const float l0 = lane < ns ? ws.part_ml[(base + lane) * 2 + 1] : 0.f;
+  float M = m0;
+  for (int c = lane + 64; c < ns; c += 64) M = fmaxf(M, ws.part_ml[(base + c) * 2]);
+  M = wave_max(M);
+  const float f0 = lane < ns ? exp2f(m0 - M) : 0.f;
+  float lsum = l0 * f0;
+  for (int c = lane + 64; c < ns; c += 64)
+    lsum = fmaf(ws.part_ml[(base + c) * 2 + 1], exp2f(ws.part_ml[(base + c) * 2] - M), lsum);
+  lsum = wave_sum(lsum);
+
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f0), u));  // 0 past ns
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = fmaf(fu, v[u][e], o[e]);
   }
-  bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
-  orow[d] = f32_to_bf16(o / lsum);
-  if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = (M + log2f(lsum)) * kLn2;
+  for (int c = kPre; c < ns; ++c) {  // long sequences only
+    const float f = exp2f(ws.part_ml[(base + c) * 2] - M);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      if (act) o[e] = fmaf(f, ws.part_o[(base + c) * D + lane * EPL + e], o[e]);
+  }
+  if (act) {
+    const float inv = 1.f / lsum;
+    bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) orow[e] = f32_to_bf16(o[e] * inv);
+  }
+  if (lane == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = (M + log2f(lsum)) * kLn2;
 }
 
 int heads_per_wg(int group) {
@@ -310,36 +371,51 @@ int heads_per_wg(int group) {
   return 1;
 }
 
+template <int D, int MUL>
+hipError_t launch_dm(const AttnParams& p, DecodeWs ws, int gs, int nsub, hipStream_t stream) {
+  const dim3 grid(ws.NS, p.Hkv * nsub, p.B), block(64 * kWaves);
+  switch (gs) {
+    case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, MUL>), grid, block, 0, stream, p, ws, nsub); break;
+    case 3: hipLaunchKernelGGL((decode_split_kernel<D, 3, MUL>), grid, block, 0, stream, p, ws, nsub); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, MUL>), grid, block, 0, stream, p, ws, nsub); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, 1, MUL>), grid, block, 0, stream, p, ws, nsub); break;
+  }
+  return hipGetLastError();
+}
+
+// Longer chunks (two q.k passes per wave) halve the partials and the fixed
+// cost per workgroup; they are used when the batch still gives at least
+// four workgroups per compute unit.
+int chunk_mul(int B, int Hkv, int nsub, int D, int max_len) {
+  const int64_t wgs = (int64_t)B * Hkv * nsub * ((max_len + chunk_keys(D, 2) - 1) / chunk_keys(D, 2));
+  return wgs >= 4 * 256 ? 2 : 1;
+}
+
 template <int D>
 hipError_t launch_d(const AttnParams& p, DecodeWs ws, hipStream_t stream) {
   const int group = p.Hq / p.Hkv;
   const int gs = heads_per_wg(group);
   const int nsub = group / gs;
-  const dim3 grid(ws.NS, p.Hkv * nsub, p.B);
-  switch (gs) {
-    case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4>), grid, dim3(256), 0, stream, p, ws, nsub); break;
-    case 3: hipLaunchKernelGGL((decode_split_kernel<D, 3>), grid, dim3(256), 0, stream, p, ws, nsub); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, dim3(256), 0, stream, p, ws, nsub); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(256), 0, stream, p, ws, nsub); break;
-  }
-  hipError_t e = hipGetLastError();
+  const int mul = chunk_mul(p.B, p.Hkv, nsub, D, p.max_len);
+  ws.chunk = chunk_keys(D, mul);
+  ws.NS = (p.max_len + ws.chunk - 1) / ws.chunk;
+  hipError_t e = mul == 2 ? launch_dm<D, 2>(p, ws, gs, nsub, stream) : launch_dm<D, 1>(p, ws, gs, nsub, stream);
   if (e != hipSuccess || ws.NS <= 1) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(p.Hq, p.B), dim3(D), 0, stream, p, ws);
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((p.B * p.Hq + 3) / 4), dim3(256), 0, stream, p, ws);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Workspace: partial outputs, then partial (max, sum) pairs.
+// Workspace: partial outputs, then partial (max, sum) pairs, sized for the
+// shorter chunks (the most partials either chunk length can produce).
 struct WsLayout {
-  int NS;
   size_t o_bytes, ml_bytes;
 };
 WsLayout ws_layout(int B, int Hq, int D, int max_len) {
   WsLayout l;
-  const int chunk = chunk_keys(D);
-  l.NS = (max_len + chunk - 1) / chunk;
-  const int64_t slots = (int64_t)B * Hq * l.NS;
+  const int chunk = chunk_keys(D, 1);
+  const int64_t slots = (int64_t)B * Hq * ((max_len + chunk - 1) / chunk);
   l.o_bytes = ((size_t)(slots * D * 4) + 255) & ~(size_t)255;
   l.ml_bytes = ((size_t)(slots * 2 * 4) + 255) & ~(size_t)255;
   return l;
@@ -353,7 +429,8 @@ size_t decode_workspace_bytes(int B, int Hq, int /*Hkv*/, int D, int max_len) {
 hipError_t launch_decode_bf16(const AttnParams& p, void* workspace, hipStream_t stream) {
   const WsLayout l = ws_layout(p.B, p.Hq, p.D, p.max_len);
   DecodeWs ws;
-  ws.NS = l.NS;
+  ws.NS = 0;     // set with the chunk length at launch
+  ws.chunk = 0;
   char* base = reinterpret_cast<char*>(workspace);
   ws.part_o = reinterpret_cast<float*>(base);
   ws.part_ml = reinterpret_cast<float*>(base + l.o_bytes);

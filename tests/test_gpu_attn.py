@@ -96,6 +96,10 @@ DECODE_CASES = [
     (4, 2, 32, [17, 24, 300], 320),
     (16, 2, 128, [900, 64], 1000),            # g=8 -> two head subgroups
     (5, 5, 64, [100, 1500], 1600),            # g=1
+    # Batches with at least 1024 workgroups of 256-key chunks take the
+    # longer-chunk kernels (64 keys per wave).
+    (8, 8, 128, [2048, 1, 255, 256, 257, 1000, 1777, 513, 64, 2047, 1500, 300, 129, 2000, 900, 1200], 2048),
+    (16, 8, 64, [2048, 17, 256, 257, 511, 512, 1999, 1024, 700, 1, 80, 1300, 1800, 640, 333, 2040], 2060),
 ]
 
 
