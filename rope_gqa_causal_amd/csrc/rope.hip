@@ -7,20 +7,20 @@
 // follows the cached-generation step of the first page's section V3: the new
 // token's q and k are rotated at its position, and its k and v join the cache.
 //
-// HBM-bound: every element is read once and written once.  A thread owns one
-// token, a run of E pairs (one 16-byte vector per half-row) and a group of
-// heads: it forms the E angles once (fp64 product and reduction modulo 2*pi,
-// fp32 sin/cos) and reuses them for every head of its group.  The number of
-// head groups is chosen per call so that a batch of few tokens (one decode
-// step) still spreads over enough threads, while a long prefill keeps whole
-// heads per thread and amortises the transcendentals over all of them.
+// HBM-bound: every element is read once and written once.  A workgroup owns
+// a few whole tokens: its threads first form the sin and cos of every pair
+// of those tokens once (fp64 product and reduction modulo 2*pi, fp32
+// sin/cos) into LDS, then walk (token, head, 16-byte chunk) units, so the
+// transcendentals are shared by all heads and a decode step of few tokens
+// still spreads over many threads.
 #include "common.h"
 #include "launch.h"
 
 namespace rgc {
 namespace {
 
-constexpr int kTargetThreads = 1 << 16;
+constexpr int kBlock = 256;
+constexpr int kTableFloats = 1024;  // sin (and cos) entries per workgroup
 
 // sin and cos of a (possibly large) angle in radians.  The product
 // position * theta and the reduction to [-pi, pi] run in fp64 with 2*pi
@@ -119,44 +119,41 @@ struct Chunk {
   }
 };
 
-// Split a flat thread index into (token, chunk, head group).
-struct Work {
-  int b, s, c, g;
-  __device__ __forceinline__ Work(int64_t gid, int S, int cpt, int ngroups) {
-    g = (int)(gid % ngroups);
-    const int64_t t = gid / ngroups;
-    c = (int)(t % cpt);
-    const int64_t tok = t / cpt;
-    s = (int)(tok % S);
-    b = (int)(tok / S);
+// Sin and cos of pair i of the workgroup's tokens, tl-major, into LDS.
+__device__ __forceinline__ void token_table(const double* theta, const int32_t* pos0, int64_t tok0, int tpb,
+                                            int64_t ntok, int S, int half, float* sn, float* cs) {
+  for (int t = threadIdx.x; t < tpb * half; t += kBlock) {
+    const int tl = t / half, i = t % half;
+    const int64_t tok = tok0 + tl;
+    if (tok >= ntok) break;
+    const int b = (int)(tok / S), s = (int)(tok % S);
+    angle_sincos((double)((pos0 ? pos0[b] : 0) + s) * theta[i], &sn[t], &cs[t]);
   }
-};
-
-template <typename T, int STYLE>
-__device__ __forceinline__ void chunk_angles(const double* theta, double pos, int c, float* sn, float* cs) {
-  constexpr int E = 16 / sizeof(T);
-#pragma unroll
-  for (int e = 0; e < E; ++e) angle_sincos(pos * theta[c * E + e], &sn[e], &cs[e]);
+  __syncthreads();
 }
 
-// Vector path of rgc_rope_apply.
+// Vector path of rgc_rope_apply: units (token, head, chunk) of tpb tokens.
 template <typename T, int STYLE>
-__global__ void __launch_bounds__(256) rope_vec_kernel(RopeParams p, int ngroups) {
+__global__ void __launch_bounds__(kBlock) rope_vec_kernel(RopeParams p, int tpb) {
   constexpr int E = 16 / sizeof(T);
-  const int cpt = p.D / (2 * E);
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)p.B * p.S * cpt * ngroups) return;
-  const Work w(gid, p.S, cpt, ngroups);
-  const int hpg = (p.H + ngroups - 1) / ngroups;
-  const int h0 = w.g * hpg, h1 = min(p.H, h0 + hpg);
-  if (h0 >= h1) return;
-  float sn[E], cs[E];
-  chunk_angles<T, STYLE>(p.theta, (double)((p.pos0 ? p.pos0[w.b] : 0) + w.s), w.c, sn, cs);
-  const Chunk<T, STYLE> ch(w.c, p.D);
-  T* base = reinterpret_cast<T*>(p.x) + (int64_t)w.b * p.sb + (int64_t)w.s * p.ss;
-  for (int h = h0; h < h1; ++h) {
-    T* row = base + (int64_t)h * p.sh;
-    ch.rotate(row, row, sn, cs);
+  __shared__ float sn_t[kTableFloats], cs_t[kTableFloats];
+  const int half = p.D / 2, cpt = p.D / (2 * E);
+  const int64_t ntok = (int64_t)p.B * p.S, tok0 = (int64_t)blockIdx.x * tpb;
+  token_table(p.theta, p.pos0, tok0, tpb, ntok, p.S, half, sn_t, cs_t);
+  const int U = p.H * cpt;
+  for (int u = threadIdx.x; u < tpb * U; u += kBlock) {
+    const int tl = u / U, h = (u % U) / cpt, c = u % cpt;
+    const int64_t tok = tok0 + tl;
+    if (tok >= ntok) break;
+    float sn[E], cs[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      sn[e] = sn_t[tl * half + c * E + e];
+      cs[e] = cs_t[tl * half + c * E + e];
+    }
+    const int b = (int)(tok / p.S), s = (int)(tok % p.S);
+    T* row = reinterpret_cast<T*>(p.x) + (int64_t)b * p.sb + (int64_t)s * p.ss + (int64_t)h * p.sh;
+    Chunk<T, STYLE>(c, p.D).rotate(row, row, sn, cs);
   }
 }
 
@@ -191,49 +188,54 @@ __global__ void __launch_bounds__(256) rope_scalar_kernel(RopeParams p) {
 // cache slot.  A cache slot outside [0, S_max) is skipped and flagged; q is
 // still rotated.
 template <typename T, int STYLE>
-__global__ void __launch_bounds__(256) rope_append_kernel(RopeAppendParams p, int ngroups) {
+__global__ void __launch_bounds__(kBlock) rope_append_kernel(RopeAppendParams p, int tpb) {
   constexpr int E = 16 / sizeof(T);
-  const int cpt = p.D / (2 * E);
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)p.B * p.S * cpt * ngroups) return;
-  const Work w(gid, p.S, cpt, ngroups);
-  const int nslots = p.Hq + 2 * p.Hkv;
-  const int hpg = (nslots + ngroups - 1) / ngroups;
-  const int h0 = w.g * hpg, h1 = min(nslots, h0 + hpg);
-  if (h0 >= h1) return;
-  const int64_t slot = (int64_t)p.pos0[w.b] + w.s;
-  const bool in_cache = slot >= 0 && slot < p.S_max;
-  if (!in_cache && p.err && w.c == 0 && h1 > p.Hq) p.err[0] = 1;
-  float sn[E], cs[E];
-  chunk_angles<T, STYLE>(p.theta, (double)slot, w.c, sn, cs);
-  const Chunk<T, STYLE> ch(w.c, p.D);
-  T* qb = reinterpret_cast<T*>(p.q) + (int64_t)w.b * p.q_sb + (int64_t)w.s * p.q_ss;
-  const T* kb = reinterpret_cast<const T*>(p.k_new) + (int64_t)w.b * p.n_sb + (int64_t)w.s * p.n_ss;
-  const T* vb = reinterpret_cast<const T*>(p.v_new) + (int64_t)w.b * p.n_sb + (int64_t)w.s * p.n_ss;
-  T* kc = reinterpret_cast<T*>(p.k_cache) + (int64_t)w.b * p.c_sb + slot * p.c_ss;
-  T* vc = reinterpret_cast<T*>(p.v_cache) + (int64_t)w.b * p.c_sb + slot * p.c_ss;
-  for (int h = h0; h < h1; ++h) {
-    if (h < p.Hq) {
-      T* row = qb + (int64_t)h * p.q_sh;
-      ch.rotate(row, row, sn, cs);
-    } else if (!in_cache) {
-      break;
-    } else if (h < p.Hq + p.Hkv) {
-      const int kh = h - p.Hq;
-      ch.rotate(kb + (int64_t)kh * p.n_sh, kc + (int64_t)kh * p.c_sh, sn, cs);
-    } else {
+  __shared__ float sn_t[kTableFloats], cs_t[kTableFloats];
+  const int half = p.D / 2, cpt = p.D / (2 * E);
+  const int64_t ntok = (int64_t)p.B * p.S, tok0 = (int64_t)blockIdx.x * tpb;
+  token_table(p.theta, p.pos0, tok0, tpb, ntok, p.S, half, sn_t, cs_t);
+  const int U = (p.Hq + 2 * p.Hkv) * cpt;
+  for (int u = threadIdx.x; u < tpb * U; u += kBlock) {
+    const int tl = u / U, h = (u % U) / cpt, c = u % cpt;
+    const int64_t tok = tok0 + tl;
+    if (tok >= ntok) break;
+    const int b = (int)(tok / p.S), s = (int)(tok % p.S);
+    const int64_t slot = (int64_t)(p.pos0 ? p.pos0[b] : 0) + s;
+    const Chunk<T, STYLE> ch(c, p.D);
+    if (h >= p.Hq && !(slot >= 0 && slot < p.S_max)) {
+      if (p.err && h == p.Hq && c == 0) p.err[0] = 1;
+      continue;
+    }
+    if (h >= p.Hq + p.Hkv) {
       const int vh = h - p.Hq - p.Hkv;
-      ch.copy(vb + (int64_t)vh * p.n_sh, vc + (int64_t)vh * p.c_sh);
+      ch.copy(reinterpret_cast<const T*>(p.v_new) + (int64_t)b * p.n_sb + (int64_t)s * p.n_ss + (int64_t)vh * p.n_sh,
+              reinterpret_cast<T*>(p.v_cache) + (int64_t)b * p.c_sb + (int64_t)vh * p.c_sh + slot * p.c_ss);
+      continue;
+    }
+    float sn[E], cs[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      sn[e] = sn_t[tl * half + c * E + e];
+      cs[e] = cs_t[tl * half + c * E + e];
+    }
+    if (h < p.Hq) {
+      T* row = reinterpret_cast<T*>(p.q) + (int64_t)b * p.q_sb + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh;
+      ch.rotate(row, row, sn, cs);
+    } else {
+      const int kh = h - p.Hq;
+      ch.rotate(reinterpret_cast<const T*>(p.k_new) + (int64_t)b * p.n_sb + (int64_t)s * p.n_ss + (int64_t)kh * p.n_sh,
+                reinterpret_cast<T*>(p.k_cache) + (int64_t)b * p.c_sb + (int64_t)kh * p.c_sh + slot * p.c_ss, sn, cs);
     }
   }
 }
 
-// Head groups per (token, chunk): enough threads to fill the GPU, whole
-// heads otherwise.
-int head_groups(int64_t token_chunks, int heads) {
-  int64_t g = (kTargetThreads + token_chunks - 1) / token_chunks;
-  if (g > heads) g = heads;
-  return g < 1 ? 1 : (int)g;
+// Tokens per workgroup: enough (token, head, chunk) units for the 256
+// threads, within the LDS table.
+int tokens_per_block(int units_per_token, int D) {
+  int t = kBlock / (units_per_token > 0 ? units_per_token : 1);
+  const int cap = kTableFloats / (D / 2);
+  if (t > cap) t = cap;
+  return t < 1 ? 1 : t;
 }
 
 template <typename T, int STYLE>
@@ -245,11 +247,9 @@ hipError_t launch_typed(const RopeParams& p, hipStream_t stream) {
                    (p.ss % E == 0) && (p.sh % E == 0);
   const int block = 256;
   if (vec) {
-    const int64_t tc = ntok * (p.D / (2 * E));
-    const int ng = head_groups(tc, p.H);
-    const int64_t n = tc * ng;
-    hipLaunchKernelGGL((rope_vec_kernel<T, STYLE>), dim3((unsigned)((n + block - 1) / block)),
-                       dim3(block), 0, stream, p, ng);
+    const int tpb = tokens_per_block(p.H * (p.D / (2 * E)), p.D);
+    hipLaunchKernelGGL((rope_vec_kernel<T, STYLE>), dim3((unsigned)((ntok + tpb - 1) / tpb)), dim3(kBlock), 0,
+                       stream, p, tpb);
   } else {
     const int64_t n = ntok * (p.D / 2);
     hipLaunchKernelGGL((rope_scalar_kernel<T, STYLE>), dim3((unsigned)((n + block - 1) / block)),
@@ -261,12 +261,10 @@ hipError_t launch_typed(const RopeParams& p, hipStream_t stream) {
 template <typename T, int STYLE>
 hipError_t launch_append_typed(const RopeAppendParams& p, hipStream_t stream) {
   constexpr int E = 16 / sizeof(T);
-  const int64_t tc = (int64_t)p.B * p.S * (p.D / (2 * E));
-  const int ng = head_groups(tc, p.Hq + 2 * p.Hkv);
-  const int64_t n = tc * ng;
-  const int block = 256;
-  hipLaunchKernelGGL((rope_append_kernel<T, STYLE>), dim3((unsigned)((n + block - 1) / block)),
-                     dim3(block), 0, stream, p, ng);
+  const int64_t ntok = (int64_t)p.B * p.S;
+  const int tpb = tokens_per_block((p.Hq + 2 * p.Hkv) * (p.D / (2 * E)), p.D);
+  hipLaunchKernelGGL((rope_append_kernel<T, STYLE>), dim3((unsigned)((ntok + tpb - 1) / tpb)), dim3(kBlock), 0,
+                     stream, p, tpb);
   return hipGetLastError();
 }
 
