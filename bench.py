@@ -45,6 +45,9 @@ def parse():
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE; both "
+                         "with --copy-calibration) into profiles/counters_*.json and exit")
     return ap.parse_args()
 
 
@@ -64,6 +67,61 @@ def stored_traffic(kind, src, launches_bytes):
     if rec.get("kernel_sha") != kernel_sha(src):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def _pmc_per_dispatch(run_dir, counter):
+    """{kernel short name: [value summed over the dispatch's instances, ...]} from a rocpd database."""
+    import glob
+    import sqlite3
+    dbs = glob.glob(os.path.join(run_dir, "**", "*.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no rocpd database under {run_dir}")
+    per = {}
+    for path in dbs:
+        rows = sqlite3.connect(path).execute(
+            "select dispatch_id, kernel_name, counter_name, value from counters_collection").fetchall()
+        for did, kname, cname, val in rows:
+            if cname != counter:
+                continue
+            short = kname.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            short = short.split("<")[0].split("::")[-1]
+            per.setdefault(short, {}).setdefault((path, did), 0.0)
+            per[short][(path, did)] += val
+    return {k: [v for _, v in sorted(d.items())] for k, d in per.items()}
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode and prefill kernels,
+    scaled by what the same counters read for a plain 1 GiB device copy."""
+    copy_bytes = float(1 << 30)
+    out = {}
+    cal = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _pmc_per_dispatch(d, counter)
+        copies = [v for k, vs in per.items() if "copy" in k.lower() for v in vs]
+        if not copies:
+            raise SystemExit(f"{counter}: no copy kernel in {d} (run with --copy-calibration)")
+        cal[counter] = copy_bytes / (max(copies) * 1024.0)
+        avg = {k: sum(vs) / len(vs) for k, vs in per.items()}
+        out[counter] = avg
+    kib = lambda c, k: out[c].get(k, 0.0)
+    def record(kind, src, kernels, note):
+        fetch = sum(kib("FETCH_SIZE", k) for k in kernels)
+        write = sum(kib("WRITE_SIZE", k) for k in kernels)
+        rec = {
+            "kernel": " + ".join(kernels), "kernel_sha": kernel_sha(src),
+            "fetch_kib_per_launch": round(fetch, 1), "write_kib_per_launch": round(write, 1),
+            "copy_scale": {"FETCH_SIZE": round(cal["FETCH_SIZE"], 4), "WRITE_SIZE": round(cal["WRITE_SIZE"], 4)},
+            "traffic_bytes_per_launch": round(fetch * 1024 * cal["FETCH_SIZE"] + write * 1024 * cal["WRITE_SIZE"]),
+            "note": note,
+        }
+        with open(os.path.join(PROFILES, f"counters_{kind}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(kind, json.dumps(rec))
+    record("decode", "decode.hip", ["decode_split_kernel", "decode_combine_kernel"],
+           "average over the 32 decode calls of one bench step (cache lengths grow by one per call)")
+    record("prefill", "prefill.hip", ["prefill_kernel"], "one prefill launch of the bench step")
 
 
 class Prefill:
@@ -162,6 +220,9 @@ def cpu_baseline(dec, seconds):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
