@@ -13,7 +13,9 @@ must read / decode-phase time, GB/s); the prefill phase's attention rate is
 reported beside it (TFLOP/s over unmasked query-key pairs).  Both are also
 given per kernel against the MI355X peaks (HBM 8 TB/s; dense bf16 MFMA
 2.5 PFLOP/s), from HIP events recorded on the stream the kernels run on.
-The fp64 CPU oracle is timed on a bounded sample of the same decode workload.
+The differential-attention variant is timed apart on its own workload
+(`diff_attn`).  The fp64 CPU oracle is timed on a bounded sample of the same
+decode workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -195,6 +197,44 @@ class Decode:
                 self.events.append((t, e0, e1))
 
 
+class Diff:
+    """Differential attention on its own workload (B 4 x 1024 tokens, 16 q /
+    8 KV heads, two maps of head dim 64, lambda 0.8); timed apart from the
+    step, since it is a variant of the prefill rather than a stage of it."""
+
+    def __init__(self, rgc, synth):
+        w = synth.WORKLOADS["diff"]
+        self.w = w
+        g = synth.generator(w.seed)
+        self.q1 = synth.normal((w.B, w.S, w.Hq, w.D), g).cuda()
+        self.q2 = synth.normal((w.B, w.S, w.Hq, w.D), g).cuda()
+        self.k1, self.k2, self.v = (synth.normal((w.B, w.Hkv, w.S, w.D), g).cuda() for _ in range(3))
+        self.o = torch.empty_like(self.q1)
+        self.rgc = rgc
+        self.flops = 2 * 4.0 * w.D * w.B * w.Hq * w.S * (w.S + 1) / 2  # two maps x unmasked pairs x 4D
+
+    def run(self):
+        self.rgc.diff_attn_prefill(self.q1, self.q2, self.k1, self.k2, self.v, self.w.lam, out=self.o)
+
+    def time(self, iters):
+        for _ in range(3):
+            self.run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            self.run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        tflops = self.flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "kernel": "diff_attn_prefill", "achieved": round(tflops, 2),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                "algorithmic_flops_per_launch": self.flops, "avg_launch_us": round(us, 3),
+                "workload": "differential attention B4 x 1024, 16q/8kv, two maps of D64, lambda 0.8, bf16",
+                "note": "timed apart from the step; FLOPs count both maps' unmasked pairs x 4D"}
+
+
 def cpu_baseline(dec, seconds):
     """Time the fp64 oracle's decode on the host: passes over the workload's
     decode calls (lengths growing by one per call, as on the GPU) until about
@@ -333,6 +373,8 @@ def main():
             "avg_launch_us": round(pk_avg * 1e3, 3),
         },
     }
+    result["diff_attn"] = Diff(rgc, synth).time(max(args.steps, 5))
+    print("[bench] timed the differential attention", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)

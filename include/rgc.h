@@ -175,6 +175,36 @@ int rgc_gqa_attn_prefill(void* o, const void* q, const void* k_cache,
                          float* lse, int32_t* err_flag, void* stream);
 
 /*
+ * rgc_diff_attn_prefill -- causal differential attention with grouped KV
+ * heads (page "750美元从零训练3个LLM：一位开发者的实战复盘", section
+ * "V2：引入前沿技术": a second attention map, weighted by lambda, is
+ * subtracted from the first to cancel common-mode noise):
+ *   o = (softmax(scale q1 K1^T) - lambda softmax(scale q2 K2^T)) V
+ * over the keys at or before each row's slot, both maps causal, query head
+ * h reading KV head h / (Hq/Hkv) for k1, k2 and v.
+ *   o          [B,Sq,Hq,D] bf16, strides (o_sb, o_ss, o_sh); written.
+ *   q1, q2     [B,Sq,Hq,D] bf16, both with strides (q_sb, q_ss, q_sh).
+ *   k1_cache, k2_cache, v_cache  [B,Hkv,S_max,D] bf16, all three with
+ *              strides (kv_sb, kv_sh, kv_ss); the value head dim equals D.
+ *   q_start    [B] int32 or NULL, as in rgc_gqa_attn_prefill.
+ *   lambda     the constant weight of the second map (no re-normalisation).
+ *   scale      applied to both maps' scores (1/sqrt(D) is the usual value).
+ * bf16 only (RGC_ERR_DTYPE otherwise); D must be 64, the head dim of each
+ * map in the differential workload (RGC_ERR_HEADDIM otherwise).  Each map is normalised by the sum of the bf16-rounded
+ * weights it multiplies V with; o is rounded once from fp32.  A row whose
+ * slots fall outside the cache gets NaN and raises *err_flag.
+ */
+int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2,
+                          const void* k1_cache, const void* k2_cache,
+                          const void* v_cache, int dtype, int B, int Sq,
+                          int Hq, int Hkv, int D, int S_max, int64_t q_sb,
+                          int64_t q_ss, int64_t q_sh, int64_t o_sb,
+                          int64_t o_ss, int64_t o_sh, int64_t kv_sb,
+                          int64_t kv_sh, int64_t kv_ss,
+                          const int32_t* q_start, float lambda, float scale,
+                          int32_t* err_flag, void* stream);
+
+/*
  * Bytes of device workspace rgc_gqa_attn_decode needs for this shape
  * (max_len: the largest length it will be called with).  0 for an invalid
  * shape.

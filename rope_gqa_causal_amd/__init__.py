@@ -13,6 +13,7 @@ the library is missing or no GPU is present, every call raises.
     rgc.kv_cache_append(kc, vc, k, v, lens)   # caches [B,Hkv,S_max,D]
     o = rgc.gqa_attn_prefill(q, kc, vc, q_start)
     o = rgc.gqa_attn_decode(q1, kc, vc, lens, max_len, ws)
+    o = rgc.diff_attn_prefill(q1, q2, k1c, k2c, vc, 0.8, q_start)
 """
 import ctypes
 import os
@@ -21,7 +22,7 @@ import torch
 
 __all__ = [
     "RgcError", "library", "rope_apply", "kv_cache_append", "rope_append", "gqa_attn_prefill",
-    "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace",
+    "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace", "diff_attn_prefill",
     "ROPE_HALF", "ROPE_INTERLEAVED",
 ]
 
@@ -48,6 +49,9 @@ _SIGNATURES = {
     "rgc_gqa_attn_prefill": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
                                   _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _p, _f, _p, _p, _p]),
+    "rgc_diff_attn_prefill": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                   _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                   _p, _f, _f, _p, _p]),
     "rgc_gqa_attn_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "rgc_gqa_attn_decode": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                  _i64, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -186,6 +190,32 @@ def gqa_attn_prefill(q, k_cache, v_cache, q_start=None, scale=None, out=None, ls
           o.stride(0), o.stride(1), o.stride(2),
           k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
           _ptr(q_start), float(scale), _ptr(lse), _ptr(err_flag), _stream(q))
+    return o
+
+
+def diff_attn_prefill(q1, q2, k1_cache, k2_cache, v_cache, lam, q_start=None, scale=None, out=None,
+                      err_flag=None):
+    """Causal differential GQA: (softmax(q1 K1^T) - lam softmax(q2 K2^T)) V.
+
+    q1, q2 [B,Sq,Hq,D] (same strides); caches [B,Hkv,S_max,D] (same strides);
+    bf16, D = 64."""
+    _gpu(q1, q2, k1_cache, k2_cache, v_cache, q_start, out, err_flag)
+    B, Sq, Hq, D = q1.shape
+    _, Hkv, S_max, _ = k1_cache.shape
+    if q2.shape != q1.shape or q2.stride() != q1.stride():
+        raise ValueError("q1 and q2 must share shape and strides")
+    if (k2_cache.shape != k1_cache.shape or v_cache.shape != k1_cache.shape
+            or k2_cache.stride() != k1_cache.stride() or v_cache.stride() != k1_cache.stride()):
+        raise ValueError("k1, k2 and v caches must share shape and strides")
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q1) if out is None else out
+    q_start = _lens(q_start, B, "q_start")
+    _call("rgc_diff_attn_prefill", _ptr(o), _ptr(q1), _ptr(q2), _ptr(k1_cache), _ptr(k2_cache),
+          _ptr(v_cache), _dtype(q1), B, Sq, Hq, Hkv, D, S_max, q1.stride(0), q1.stride(1), q1.stride(2),
+          o.stride(0), o.stride(1), o.stride(2),
+          k1_cache.stride(0), k1_cache.stride(1), k1_cache.stride(2),
+          _ptr(q_start), float(lam), float(scale), _ptr(err_flag), _stream(q1))
     return o
 
 

@@ -75,6 +75,16 @@ struct AttnParams {
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, bool decode, hipStream_t stream);
 
+// Differential attention: q / k / v / o of `a` are q1, k1 cache, v cache
+// and o; q2 and k2 share the strides of q1 and k1.
+struct DiffParams {
+  AttnParams a;
+  const void* q2;
+  const void* k2;
+  float lambda;
+};
+hipError_t launch_diff_bf16(const DiffParams& p, hipStream_t stream);
+
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len);
 hipError_t launch_decode_bf16(const AttnParams& p, void* ws, hipStream_t stream);
 

@@ -35,12 +35,13 @@
 //    issued heaviest q-tile first.
 #include "common.h"
 #include "launch.h"
+#include "mfma_attn.h"
 
 namespace rgc {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = kAttnLog2e;
+constexpr float kLn2 = kAttnLn2;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;   // query positions per workgroup
@@ -48,29 +49,6 @@ constexpr int kKT = 64;            // keys per tile
 constexpr int kSlots = 3;          // LDS ring: tile j read, j+1 ready, j+2 written
 constexpr int kXcds = 8;           // MI355X: workgroup i is dispatched to XCD i % 8
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// max / sum of x[lane] and x[lane ^ 32] with one v_permlane32_swap: the swap
-// hands each half the other half's value in one of its two results.
-__device__ __forceinline__ float max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // LDS layout: kSlots K tiles, then kSlots V tiles, each row-major
 // [64 keys][D] in 16-byte chunks; chunk c of row r sits at chunk c ^ swz(r).
@@ -160,19 +138,6 @@ __device__ __forceinline__ void store_tile(const u32x4 (&st)[Tile<D>::LOADS], co
     *reinterpret_cast<u32x4*>(lds + sg.loff[i] + SLOT * T::MAT_BYTES) = st[i];
 }
 
-// V^T fragment: two transposed 8-byte reads.  In each 16-lane group (h =
-// lane/32 picks the key half, (lane/16)%2 the 16-row half of the d block)
-// lane x supplies the address of 4 consecutive d of key 16kk + 4h + x/4 (+8
-// for the second read); lane j then holds those 4 keys' values at
-// d = 32db + lane%32 -- the MFMA A-operand layout.
-template <int D>
-__device__ __forceinline__ u32x4 vt_frag(const char* a) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * Tile<D>::ROW_BYTES));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  return u32x4{l2[0], l2[1], h2[0], h2[1]};
-}
-
 template <int D>
 struct WaveCtx {
   u32x4 qf[D / 16];          // Q^T fragments (B operand)
@@ -259,7 +224,7 @@ __device__ __forceinline__ void compute_tile(WaveCtx<D>& w, int j0) {
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int q = 0; q < DB; ++q)
-      w.acc_o[q] = mfma(vt_frag<D>(w.vp[q] + SLOT * T::MAT_BYTES + kk * 16 * T::ROW_BYTES), pf[kk], w.acc_o[q]);
+      w.acc_o[q] = mfma(vt_frag<T::ROW_BYTES>(w.vp[q] + SLOT * T::MAT_BYTES + kk * 16 * T::ROW_BYTES), pf[kk], w.acc_o[q]);
 }
 
 // One step of the ring for tile jt in slot SLOT: fetch tile jt+2, multiply

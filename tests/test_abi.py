@@ -26,8 +26,9 @@ def _declared():
 def test_header_symbols_are_exported():
     lib = rgc.library()
     names = _declared()
-    assert {"rgc_rope_apply", "rgc_kv_cache_append", "rgc_gqa_attn_prefill",
-            "rgc_gqa_attn_decode", "rgc_gqa_attn_decode_workspace_size"} <= set(names)
+    assert {"rgc_rope_apply", "rgc_kv_cache_append", "rgc_rope_append", "rgc_gqa_attn_prefill",
+            "rgc_gqa_attn_decode", "rgc_gqa_attn_decode_workspace_size",
+            "rgc_diff_attn_prefill"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -64,6 +65,29 @@ def test_prefill_rejects_bad_arguments_before_launch():
     assert _prefill(scale=float("nan")) == -10
     assert _prefill(B=0) == OK                      # empty batch: a no-op
     assert _prefill(Sq=0) == OK
+
+
+def _diff(**kw):
+    a = dict(o=A, q1=A, q2=A, k1=A, k2=A, v=A, dt=BF16, B=2, Sq=16, Hq=4, Hkv=2, D=64, S_max=16,
+             q_sb=16 * 4 * 64, q_ss=4 * 64, q_sh=64, o_sb=16 * 4 * 64, o_ss=4 * 64, o_sh=64,
+             kv_sb=2 * 16 * 64, kv_sh=16 * 64, kv_ss=64, q_start=None, lam=0.8, scale=0.125, err=None)
+    a.update(kw)
+    return rgc.library().rgc_diff_attn_prefill(
+        a["o"], a["q1"], a["q2"], a["k1"], a["k2"], a["v"], a["dt"], a["B"], a["Sq"], a["Hq"], a["Hkv"],
+        a["D"], a["S_max"], a["q_sb"], a["q_ss"], a["q_sh"], a["o_sb"], a["o_ss"], a["o_sh"],
+        a["kv_sb"], a["kv_sh"], a["kv_ss"], a["q_start"], a["lam"], a["scale"], a["err"], None)
+
+
+def test_diff_rejects_bad_arguments_before_launch():
+    assert _diff(Hq=3) == GROUP
+    assert _diff(dt=F32) == DTYPE        # bf16 only
+    assert _diff(D=128) == HEADDIM       # head dim 64 only
+    assert _diff(q2=None) == NULL
+    assert _diff(k2=A + 8) == LAYOUT
+    assert _diff(Sq=17) == CAPACITY
+    assert _diff(lam=float("inf")) == -10
+    assert _diff(B=0) == OK
+    assert _diff(Sq=0) == OK
 
 
 def _decode(**kw):
