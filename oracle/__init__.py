@@ -34,6 +34,8 @@ def _load():
         lib.orc_bf16_bits.argtypes = [_c_d]
         lib.orc_rope_f64.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_i64, _c_i64, _c_i64, _c_p, _c_d, _c_int]
+        lib.orc_norm_rope_f64.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                          _c_i64, _c_i64, _c_i64, _c_p, _c_d, _c_int, _c_d]
         lib.orc_rope_apply.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_i64, _c_i64, _c_i64, _c_p, _c_d, _c_int]
         lib.orc_kv_cache_append.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -110,6 +112,18 @@ def rope_f64(x, pos0=None, base=10000.0, style=ROPE_HALF):
     p, pp = _i32(pos0, B)
     _check(_load().orc_rope_f64(out.data_ptr(), x.data_ptr(), _dt(x), B, S, H, D,
                                 x.stride(0), x.stride(1), x.stride(2), pp, base, style))
+    return out
+
+
+def norm_rope_f64(x, pos0=None, base=10000.0, style=ROPE_HALF, eps=1e-6):
+    """Exact (double) QK normalisation then RoPE of x [B,S,H,D]: each head
+    vector divided by sqrt(mean of squares + eps), then rotated."""
+    x = _cpu(x)
+    B, S, H, D = x.shape
+    out = torch.empty((B, S, H, D), dtype=torch.float64)
+    p, pp = _i32(pos0, B)
+    _check(_load().orc_norm_rope_f64(out.data_ptr(), x.data_ptr(), _dt(x), B, S, H, D,
+                                     x.stride(0), x.stride(1), x.stride(2), pp, base, style, eps))
     return out
 
 

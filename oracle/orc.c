@@ -122,6 +122,57 @@ int orc_rope_apply(void* x, int dt, int B, int S, int H, int D, int64_t sb,
   return ORC_OK;
 }
 
+/* ---- QK normalisation before RoPE ----------------------------------------- */
+
+/*
+ * RMS normalisation of one head vector ([P2] core architecture: RMSNorm
+ * replaces LayerNorm; [P3] 设置: the model normalises q and k): the vector is
+ * divided by the root of the mean of its squares plus eps.  No learned weight
+ * (the pages print none).  Then the rotation of rope_vec, on the normalised
+ * values.
+ */
+static void norm_rope_vec(double* out, double* y, const void* x, int dt, int64_t off, int D,
+                          double pos, double base, int style, double eps) {
+  double ss = 0.0;
+  for (int d = 0; d < D; ++d) {
+    double v = load(x, dt, off + d);
+    y[d] = v;
+    ss += v * v;
+  }
+  double r = 1.0 / sqrt(ss / (double)D + eps);
+  for (int d = 0; d < D; ++d) y[d] *= r;
+  int half = D / 2;
+  for (int i = 0; i < half; ++i) {
+    double theta = pow(base, -2.0 * (double)i / (double)D);
+    double ang = pos * theta;
+    double c = cos(ang), s = sin(ang);
+    int ia = (style == ORC_ROPE_HALF) ? i : 2 * i;
+    int ib = (style == ORC_ROPE_HALF) ? i + half : 2 * i + 1;
+    double a = y[ia], b = y[ib];
+    out[ia] = a * c - b * s;
+    out[ib] = a * s + b * c;
+  }
+}
+
+int orc_norm_rope_f64(double* out, const void* x, int dt, int B, int S, int H,
+                      int D, int64_t sb, int64_t ss, int64_t sh,
+                      const int32_t* pos0, double base, int style, double eps) {
+  if (!rope_args_ok(dt, B, S, H, D, style) || !(eps >= 0.0)) return ORC_ERR_ARG;
+  double* y = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!y) return ORC_ERR_ARG;
+  for (int b = 0; b < B; ++b)
+    for (int s = 0; s < S; ++s) {
+      double pos = (double)((pos0 ? pos0[b] : 0) + s);
+      for (int h = 0; h < H; ++h) {
+        int64_t off = (int64_t)b * sb + (int64_t)s * ss + (int64_t)h * sh;
+        double* dst = out + (((int64_t)b * S + s) * H + h) * D;
+        norm_rope_vec(dst, y, x, dt, off, D, pos, base, style, eps);
+      }
+    }
+  free(y);
+  return ORC_OK;
+}
+
 /* ---- cache append -------------------------------------------------------- */
 
 /* [P1] V3 and [P2]: the cache keeps every step's K and V rows in order. */

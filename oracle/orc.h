@@ -80,6 +80,16 @@ int orc_rope_f64(double* out, const void* x, int dt, int B, int S, int H,
                  int D, int64_t sb, int64_t ss, int64_t sh,
                  const int32_t* pos0, double base, int style);
 
+/*
+ * QK normalisation then RoPE, unrounded: each head vector is divided by
+ * sqrt(mean of its squares + eps) (no weight), then rotated as by
+ * orc_rope_f64.  Same layout and out as orc_rope_f64.  Follows [P2] (RMSNorm)
+ * and [P3] 设置 (q and k are normalised).
+ */
+int orc_norm_rope_f64(double* out, const void* x, int dt, int B, int S, int H,
+                      int D, int64_t sb, int64_t ss, int64_t sh,
+                      const int32_t* pos0, double base, int style, double eps);
+
 /* RoPE in place: the exact double result rounded once to dt. */
 int orc_rope_apply(void* x, int dt, int B, int S, int H, int D, int64_t sb,
                    int64_t ss, int64_t sh, const int32_t* pos0, double base,
