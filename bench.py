@@ -235,6 +235,34 @@ class Diff:
                 "note": "timed apart from the step; FLOPs count both maps' unmasked pairs x 4D"}
 
 
+def time_prologues(pre, iters):
+    """The fused prologue on the 3.8B-shaped prefill batch, plain and with QK
+    normalisation (HBM-bound: q, k, v read once; q and the cache rows written
+    once)."""
+    w = pre.w
+    byts = 2.0 * 2 * w.B * w.S * (w.Hq + 2 * w.Hkv) * w.D  # bf16 read + write
+    out = {}
+    for name, fn in (("rope_append", lambda: pre.rgc.rope_append(pre.q, pre.k, pre.v, pre.kc, pre.vc, pre.pos0)),
+                     ("norm_rope_append", lambda: pre.rgc.norm_rope_append(pre.q, pre.k, pre.v, pre.kc, pre.vc,
+                                                                          pre.pos0, eps=1e-6))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        out[name] = {"avg_launch_us": round(us, 3), "achieved": round(byts / (us * 1e-6) / 1e9, 1), "unit": "GB/s",
+                     "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    out["bound"] = "hbm"
+    out["algorithmic_bytes_per_launch"] = byts
+    out["workload"] = "B8 x 2048 tokens, 24 q / 8 kv heads, D128, bf16 (q rotated in place; k, v into the cache)"
+    return out
+
+
 def cpu_baseline(dec, seconds):
     """Time the fp64 oracle's decode on the host: passes over the workload's
     decode calls (lengths growing by one per call, as on the GPU) until about
@@ -374,6 +402,7 @@ def main():
         },
     }
     result["diff_attn"] = Diff(rgc, synth).time(max(args.steps, 5))
+    result["prologue"] = time_prologues(pre, max(args.steps, 5))
     print("[bench] timed the differential attention", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -147,6 +147,22 @@ int rgc_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache
                     void* stream);
 
 /*
+ * rgc_norm_rope_append -- rgc_rope_append with QK normalisation first: each
+ * q and k head vector is divided by sqrt(mean of its D squares + eps) before
+ * it is rotated (RMS normalisation: page "从零手训LLaMa：125M模型11小时训练
+ * 全记录", core-architecture section; q and k normalised: page "训练3.8B
+ * LLM至0.384 CORE，成本998美元 – Hugo Vergnes", section 设置).  No learned
+ * weight (the pages print none); v is copied unchanged.  Arguments as for
+ * rgc_rope_append, plus eps >= 0 (finite; RGC_ERR_ARG otherwise).  The sum
+ * of squares and the rotation run in fp32; the result is rounded once.
+ */
+int rgc_norm_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         int dtype, int B, int S, int Hq, int Hkv, int D, int S_max, int64_t q_sb,
+                         int64_t q_ss, int64_t q_sh, int64_t sb, int64_t ss, int64_t sh, int64_t c_sb,
+                         int64_t c_sh, int64_t c_ss, const int32_t* pos0, double base, int style,
+                         float eps, int32_t* err_flag, void* stream);
+
+/*
  * rgc_gqa_attn_prefill -- causal GQA attention of a block of query rows over
  * the cache.
  *   o        [B,Sq,Hq,D] of dtype, strides (o_sb, o_ss, o_sh); written.

@@ -21,7 +21,8 @@ import os
 import torch
 
 __all__ = [
-    "RgcError", "library", "rope_apply", "kv_cache_append", "rope_append", "gqa_attn_prefill",
+    "RgcError", "library", "rope_apply", "kv_cache_append", "rope_append", "norm_rope_append",
+    "gqa_attn_prefill",
     "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace", "diff_attn_prefill",
     "ROPE_HALF", "ROPE_INTERLEAVED",
 ]
@@ -46,6 +47,8 @@ _SIGNATURES = {
                                  _i64, _i64, _i64, _p, _p, _p]),
     "rgc_rope_append": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64,
                              _i64, _i64, _i64, _i64, _i64, _i64, _p, _d, _i, _p, _p]),
+    "rgc_norm_rope_append": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64,
+                                  _i64, _i64, _i64, _i64, _i64, _i64, _p, _d, _i, _f, _p, _p]),
     "rgc_gqa_attn_prefill": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
                                   _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _p, _f, _p, _p, _p]),
@@ -149,11 +152,7 @@ def kv_cache_append(k_cache, v_cache, k_new, v_new, pos0, err_flag=None):
           _ptr(err_flag), _stream(k_cache))
 
 
-def rope_append(q, k_new, v_new, k_cache, v_cache, pos0, base=10000.0, style=ROPE_HALF, err_flag=None):
-    """Fused step prologue: rotate q in place and k_new into the caches, copy v_new.
-
-    q [B,S,Hq,D]; k_new, v_new [B,S,Hkv,D]; caches [B,Hkv,S_max,D]; token (b,s)
-    has position and cache slot pos0[b] + s."""
+def _rope_append_args(q, k_new, v_new, k_cache, v_cache, pos0, err_flag):
     _gpu(q, k_new, v_new, k_cache, v_cache, pos0, err_flag)
     B, S, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
@@ -162,11 +161,27 @@ def rope_append(q, k_new, v_new, k_cache, v_cache, pos0, base=10000.0, style=ROP
     if tuple(k_new.shape) != (B, S, Hkv, D) or v_new.shape != k_new.shape:
         raise ValueError("new rows must be [B,S,Hkv,D]")
     pos0 = _lens(pos0, B, "pos0")
-    _call("rgc_rope_append", _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _dtype(q),
-          B, S, Hq, Hkv, D, S_max, q.stride(0), q.stride(1), q.stride(2),
-          k_new.stride(0), k_new.stride(1), k_new.stride(2),
-          k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
-          _ptr(pos0), float(base), int(style), _ptr(err_flag), _stream(q))
+    return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _dtype(q),
+            B, S, Hq, Hkv, D, S_max, q.stride(0), q.stride(1), q.stride(2),
+            k_new.stride(0), k_new.stride(1), k_new.stride(2),
+            k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), _ptr(pos0))
+
+
+def rope_append(q, k_new, v_new, k_cache, v_cache, pos0, base=10000.0, style=ROPE_HALF, err_flag=None):
+    """Fused step prologue: rotate q in place and k_new into the caches, copy v_new.
+
+    q [B,S,Hq,D]; k_new, v_new [B,S,Hkv,D]; caches [B,Hkv,S_max,D]; token (b,s)
+    has position and cache slot pos0[b] + s."""
+    args = _rope_append_args(q, k_new, v_new, k_cache, v_cache, pos0, err_flag)
+    _call("rgc_rope_append", *args, float(base), int(style), _ptr(err_flag), _stream(q))
+    return q
+
+
+def norm_rope_append(q, k_new, v_new, k_cache, v_cache, pos0, base=10000.0, style=ROPE_HALF, eps=1e-6,
+                     err_flag=None):
+    """rope_append with each q and k head vector first divided by sqrt(mean square + eps)."""
+    args = _rope_append_args(q, k_new, v_new, k_cache, v_cache, pos0, err_flag)
+    _call("rgc_norm_rope_append", *args, float(base), int(style), float(eps), _ptr(err_flag), _stream(q))
     return q
 
 

@@ -110,15 +110,19 @@ int rgc_kv_cache_append(void* k_cache, void* v_cache, int dtype, int B, int Hkv,
   return hip_status(launch_append(p, dtype, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int rgc_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, int dtype,
-                    int B, int S, int Hq, int Hkv, int D, int S_max, int64_t q_sb, int64_t q_ss, int64_t q_sh,
-                    int64_t sb, int64_t ss, int64_t sh, int64_t c_sb, int64_t c_sh, int64_t c_ss,
-                    const int32_t* pos0, double base, int style, int32_t* err_flag, void* stream) {
+namespace {
+
+int rope_append_impl(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, int dtype,
+                     int B, int S, int Hq, int Hkv, int D, int S_max, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                     int64_t sb, int64_t ss, int64_t sh, int64_t c_sb, int64_t c_sh, int64_t c_ss,
+                     const int32_t* pos0, double base, int style, bool norm, float eps, int32_t* err_flag,
+                     void* stream) {
   if (!dtype_ok(dtype)) return RGC_ERR_DTYPE;
   if (B < 0 || S < 0 || Hq < 0 || Hkv < 0 || D < 0 || S_max < 0) return RGC_ERR_SHAPE;
   if (!headdim_ok(D)) return RGC_ERR_HEADDIM;
   if (style != RGC_ROPE_HALF && style != RGC_ROPE_INTERLEAVED) return RGC_ERR_ARG;
   if (!(base > 0.0) || !std::isfinite(base)) return RGC_ERR_ARG;
+  if (norm && !(eps >= 0.f && std::isfinite(eps))) return RGC_ERR_ARG;
   if (B == 0 || S == 0 || (Hq == 0 && Hkv == 0)) return RGC_OK;
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !pos0) return RGC_ERR_NULL;
   if (S > S_max) return RGC_ERR_CAPACITY;
@@ -151,9 +155,29 @@ int rgc_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache
   p.c_ss = c_ss;
   p.pos0 = pos0;
   p.err = err_flag;
+  p.eps = eps;
   for (int i = 0; i < kMaxRopeDim / 2; ++i)
     p.theta[i] = i < D / 2 ? std::pow(base, -2.0 * (double)i / (double)D) : 0.0;
-  return hip_status(launch_rope_append(p, dtype, style, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(launch_rope_append(p, dtype, style, norm, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int rgc_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, int dtype,
+                    int B, int S, int Hq, int Hkv, int D, int S_max, int64_t q_sb, int64_t q_ss, int64_t q_sh,
+                    int64_t sb, int64_t ss, int64_t sh, int64_t c_sb, int64_t c_sh, int64_t c_ss,
+                    const int32_t* pos0, double base, int style, int32_t* err_flag, void* stream) {
+  return rope_append_impl(q, k_new, v_new, k_cache, v_cache, dtype, B, S, Hq, Hkv, D, S_max, q_sb, q_ss, q_sh, sb,
+                          ss, sh, c_sb, c_sh, c_ss, pos0, base, style, false, 0.f, err_flag, stream);
+}
+
+int rgc_norm_rope_append(void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, int dtype,
+                         int B, int S, int Hq, int Hkv, int D, int S_max, int64_t q_sb, int64_t q_ss,
+                         int64_t q_sh, int64_t sb, int64_t ss, int64_t sh, int64_t c_sb, int64_t c_sh,
+                         int64_t c_ss, const int32_t* pos0, double base, int style, float eps,
+                         int32_t* err_flag, void* stream) {
+  return rope_append_impl(q, k_new, v_new, k_cache, v_cache, dtype, B, S, Hq, Hkv, D, S_max, q_sb, q_ss, q_sh, sb,
+                          ss, sh, c_sb, c_sh, c_ss, pos0, base, style, true, eps, err_flag, stream);
 }
 
 namespace {

@@ -37,9 +37,10 @@ struct RopeAppendParams {
   int64_t c_sb, c_sh, c_ss;
   const int32_t* pos0;
   int32_t* err;
+  float eps;                      // QK normalisation (used by the normalising variant)
   double theta[kMaxRopeDim / 2];
 };
-hipError_t launch_rope_append(const RopeAppendParams& p, int dtype, int style, hipStream_t stream);
+hipError_t launch_rope_append(const RopeAppendParams& p, int dtype, int style, bool norm, hipStream_t stream);
 
 struct AppendParams {
   void* k_cache;

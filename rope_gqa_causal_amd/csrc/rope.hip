@@ -74,7 +74,12 @@ struct Chunk {
       : off0(STYLE == ROPE_HALF ? c * E : 2 * c * E), off1(STYLE == ROPE_HALF ? D / 2 + c * E : 2 * c * E + E) {}
 
   // dst[off0, off1] = rotation of src[off0, off1] by the chunk's angles.
-  __device__ __forceinline__ void rotate(const T* src, T* dst, const float* sn, const float* cs) const {
+  // With NORM the head vector is first divided by sqrt(mean of squares +
+  // eps): the cpt lanes that hold one row (adjacent, a power of two, aligned)
+  // add their sums of squares with xor shuffles.
+  template <bool NORM = false>
+  __device__ __forceinline__ void rotate(const T* src, T* dst, const float* sn, const float* cs, int cpt = 1,
+                                         float inv_d = 0.f, float eps = 0.f) const {
     u32x4 v0 = ld16(src + off0);
     u32x4 v1 = ld16(src + off1);
     float a[E], bb[E];
@@ -91,6 +96,18 @@ struct Chunk {
         bb[e] = Elem<T>::get(v0, 2 * e + 1);
         a[E / 2 + e] = Elem<T>::get(v1, 2 * e);
         bb[E / 2 + e] = Elem<T>::get(v1, 2 * e + 1);
+      }
+    }
+    if (NORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss = fmaf(a[e], a[e], fmaf(bb[e], bb[e], ss));
+      for (int m = 1; m < cpt; m <<= 1) ss += __shfl_xor(ss, m, 64);
+      const float r = 1.f / sqrtf(fmaf(ss, inv_d, eps));
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        a[e] *= r;
+        bb[e] *= r;
       }
     }
     float w0[E], w1[E];
@@ -185,9 +202,12 @@ __global__ void __launch_bounds__(256) rope_scalar_kernel(RopeParams p) {
 
 // Fused prologue: head slots [0, Hq) rotate q in place, [Hq, Hq+Hkv) rotate
 // the new k into its cache slot, [Hq+Hkv, Hq+2Hkv) copy the new v into its
-// cache slot.  A cache slot outside [0, S_max) is skipped and flagged; q is
-// still rotated.
-template <typename T, int STYLE>
+// cache slot.  With NORM, q and k head vectors are RMS-normalised first (QK
+// norm: page "训练3.8B LLM至0.384 CORE，成本998美元 – Hugo Vergnes", section
+// 设置; RMSNorm: page "从零手训LLaMa：125M模型11小时训练全记录",
+// core-architecture section).  A cache slot outside [0, S_max) is skipped and
+// flagged; q is still rotated.
+template <typename T, int STYLE, bool NORM>
 __global__ void __launch_bounds__(kBlock) rope_append_kernel(RopeAppendParams p, int tpb) {
   constexpr int E = 16 / sizeof(T);
   __shared__ float sn_t[kTableFloats], cs_t[kTableFloats];
@@ -218,13 +238,16 @@ __global__ void __launch_bounds__(kBlock) rope_append_kernel(RopeAppendParams p,
       sn[e] = sn_t[tl * half + c * E + e];
       cs[e] = cs_t[tl * half + c * E + e];
     }
+    const float inv_d = 1.f / (float)p.D;
     if (h < p.Hq) {
       T* row = reinterpret_cast<T*>(p.q) + (int64_t)b * p.q_sb + (int64_t)s * p.q_ss + (int64_t)h * p.q_sh;
-      ch.rotate(row, row, sn, cs);
+      ch.template rotate<NORM>(row, row, sn, cs, cpt, inv_d, p.eps);
     } else {
       const int kh = h - p.Hq;
-      ch.rotate(reinterpret_cast<const T*>(p.k_new) + (int64_t)b * p.n_sb + (int64_t)s * p.n_ss + (int64_t)kh * p.n_sh,
-                reinterpret_cast<T*>(p.k_cache) + (int64_t)b * p.c_sb + (int64_t)kh * p.c_sh + slot * p.c_ss, sn, cs);
+      ch.template rotate<NORM>(
+          reinterpret_cast<const T*>(p.k_new) + (int64_t)b * p.n_sb + (int64_t)s * p.n_ss + (int64_t)kh * p.n_sh,
+          reinterpret_cast<T*>(p.k_cache) + (int64_t)b * p.c_sb + (int64_t)kh * p.c_sh + slot * p.c_ss, sn, cs, cpt,
+          inv_d, p.eps);
     }
   }
 }
@@ -259,12 +282,15 @@ hipError_t launch_typed(const RopeParams& p, hipStream_t stream) {
 }
 
 template <typename T, int STYLE>
-hipError_t launch_append_typed(const RopeAppendParams& p, hipStream_t stream) {
+hipError_t launch_append_typed(const RopeAppendParams& p, bool norm, hipStream_t stream) {
   constexpr int E = 16 / sizeof(T);
   const int64_t ntok = (int64_t)p.B * p.S;
   const int tpb = tokens_per_block((p.Hq + 2 * p.Hkv) * (p.D / (2 * E)), p.D);
-  hipLaunchKernelGGL((rope_append_kernel<T, STYLE>), dim3((unsigned)((ntok + tpb - 1) / tpb)), dim3(kBlock), 0,
-                     stream, p, tpb);
+  const dim3 grid((unsigned)((ntok + tpb - 1) / tpb));
+  if (norm)
+    hipLaunchKernelGGL((rope_append_kernel<T, STYLE, true>), grid, dim3(kBlock), 0, stream, p, tpb);
+  else
+    hipLaunchKernelGGL((rope_append_kernel<T, STYLE, false>), grid, dim3(kBlock), 0, stream, p, tpb);
   return hipGetLastError();
 }
 
@@ -278,12 +304,12 @@ hipError_t launch_rope(const RopeParams& p, int dtype, int style, hipStream_t st
                             : launch_typed<bf16_t, ROPE_INTERLEAVED>(p, stream);
 }
 
-hipError_t launch_rope_append(const RopeAppendParams& p, int dtype, int style, hipStream_t stream) {
+hipError_t launch_rope_append(const RopeAppendParams& p, int dtype, int style, bool norm, hipStream_t stream) {
   if (dtype == DT_F32)
-    return style == ROPE_HALF ? launch_append_typed<float, ROPE_HALF>(p, stream)
-                              : launch_append_typed<float, ROPE_INTERLEAVED>(p, stream);
-  return style == ROPE_HALF ? launch_append_typed<bf16_t, ROPE_HALF>(p, stream)
-                            : launch_append_typed<bf16_t, ROPE_INTERLEAVED>(p, stream);
+    return style == ROPE_HALF ? launch_append_typed<float, ROPE_HALF>(p, norm, stream)
+                              : launch_append_typed<float, ROPE_INTERLEAVED>(p, norm, stream);
+  return style == ROPE_HALF ? launch_append_typed<bf16_t, ROPE_HALF>(p, norm, stream)
+                            : launch_append_typed<bf16_t, ROPE_INTERLEAVED>(p, norm, stream);
 }
 
 }  // namespace rgc

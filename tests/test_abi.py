@@ -26,7 +26,8 @@ def _declared():
 def test_header_symbols_are_exported():
     lib = rgc.library()
     names = _declared()
-    assert {"rgc_rope_apply", "rgc_kv_cache_append", "rgc_rope_append", "rgc_gqa_attn_prefill",
+    assert {"rgc_rope_apply", "rgc_kv_cache_append", "rgc_rope_append", "rgc_norm_rope_append",
+            "rgc_gqa_attn_prefill",
             "rgc_gqa_attn_decode", "rgc_gqa_attn_decode_workspace_size",
             "rgc_diff_attn_prefill"} <= set(names)
     for n in names:

@@ -131,3 +131,45 @@ def test_rope_append_matches_the_oracle_and_flags_capacity():
     written = ~torch.isnan(want)
     assert torch.equal(torch.isnan(got), torch.isnan(want))          # same slots written
     assert (got[written].double() - want[written].double()).abs().max().item() <= 2 ** -7 * 4
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("style", [rgc.ROPE_HALF, rgc.ROPE_INTERLEAVED])
+@pytest.mark.parametrize("S,D", [(1, 128), (19, 64), (5, 32)])
+def test_norm_rope_append_matches_the_oracle(dtype, style, S, D):
+    B, Hq, Hkv, S_max, eps = 3, 6, 2, 64, 1e-6
+    g = synth.generator(300 + S * D + style)
+    q, k, v = synth.qkv(B, S, Hq, Hkv, D, g, dtype)
+    q = q * 3.0  # away from unit scale, so the normalisation matters
+    pos0 = torch.tensor([0, 17, S_max - S], dtype=torch.int32)
+    ref_q = oracle.norm_rope_f64(q, pos0, 10000.0, style, eps)
+    ref_k = oracle.norm_rope_f64(k, pos0, 10000.0, style, eps)
+    qg = q.cuda()
+    kc, vc = [t.cuda() for t in synth.nan_cache(B, Hkv, S_max, D, dtype)]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rgc.norm_rope_append(qg, k.cuda(), v.cuda(), kc, vc, pos0.cuda(), 10000.0, style, eps, err_flag=err)
+    assert err.item() == 0
+    assert_close(qg, ref_q, dtype, "normalised rope q")
+    ibits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    kc, vc = kc.cpu(), vc.cpu()
+    for b in range(B):
+        sl = slice(int(pos0[b]), int(pos0[b]) + S)
+        assert_close(kc[b, :, sl].transpose(0, 1), ref_k[b], dtype, "normalised rope k in cache")
+        assert torch.equal(vc[b, :, sl].transpose(0, 1).contiguous().view(ibits), v[b].contiguous().view(ibits))
+    outside = torch.ones(S_max, dtype=torch.bool)
+    for b in range(B):
+        m = outside.clone()
+        m[int(pos0[b]):int(pos0[b]) + S] = False
+        assert torch.isnan(kc[b, :, m].float()).all() and torch.isnan(vc[b, :, m].float()).all()
+
+
+def test_norm_rope_append_of_zero_rows_is_zero_and_plain_prologue_is_unchanged():
+    B, S, Hq, Hkv, D, S_max = 2, 3, 4, 2, 64, 16
+    z = torch.zeros(B, S, Hq, D, dtype=torch.bfloat16, device="cuda")
+    zk = torch.zeros(B, S, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    kc = torch.full((B, Hkv, S_max, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = kc.clone()
+    pos0 = torch.tensor([0, 5], dtype=torch.int32, device="cuda")
+    rgc.norm_rope_append(z, zk, zk, kc, vc, pos0, eps=1e-6)
+    assert torch.equal(z, torch.zeros_like(z))
+    assert torch.equal(kc[0, :, :S], torch.zeros(Hkv, S, D, dtype=torch.bfloat16, device="cuda"))
