@@ -13,8 +13,9 @@ must read / decode-phase time, GB/s); the prefill phase's attention rate is
 reported beside it (TFLOP/s over unmasked query-key pairs).  Both are also
 given per kernel against the MI355X peaks (HBM 8 TB/s; dense bf16 MFMA
 2.5 PFLOP/s), from HIP events recorded on the stream the kernels run on.
-The differential-attention variant is timed apart on its own workload
-(`diff_attn`).  The fp64 CPU oracle is timed on a bounded sample of the same
+The differential-attention variant (`diff_attn`), the packed-document prefill
+(`varlen_prefill`) and the fused prologue with and without QK normalisation
+(`prologue`) are timed apart on their own workloads.  The fp64 CPU oracle is timed on a bounded sample of the same
 decode workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -235,6 +236,44 @@ class Diff:
                 "note": "timed apart from the step; FLOPs count both maps' unmasked pairs x 4D"}
 
 
+class Varlen:
+    """Document-masked prefill on the 3.8B-shaped token count: 16384 tokens
+    packed as documents of 64..4096 tokens, 24 q / 8 KV heads, D 128."""
+
+    def __init__(self, rgc, synth):
+        w = synth.WORKLOADS["varlen"]
+        g = synth.generator(w.seed)
+        self.lens = synth.document_lengths(w.S, w.len_lo, w.len_hi, g)
+        self.cu = torch.cat([torch.zeros(1, dtype=torch.int32), self.lens.cumsum(0).to(torch.int32)]).cuda()
+        self.q = synth.normal((w.S, w.Hq, w.D), g).cuda()
+        self.k = synth.normal((w.S, w.Hkv, w.D), g).cuda()
+        self.v = synth.normal((w.S, w.Hkv, w.D), g).cuda()
+        self.o = torch.empty_like(self.q)
+        self.max_len = int(self.lens.max())
+        n = self.lens.to(torch.float64)
+        self.flops = float((n * (n + 1) / 2).sum()) * w.Hq * 4.0 * w.D
+        self.rgc, self.w = rgc, w
+
+    def time(self, iters):
+        run = lambda: self.rgc.gqa_attn_prefill_varlen(self.q, self.k, self.v, self.cu, self.max_len, out=self.o)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        tf = self.flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "kernel": "gqa_attn_prefill_varlen", "achieved": round(tf, 2),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                "algorithmic_flops_per_launch": self.flops, "avg_launch_us": round(us, 3),
+                "documents": int(self.lens.numel()),
+                "workload": "16384 tokens packed as documents of U{64..4096} tokens, 24q/8kv, D128, bf16"}
+
+
 def time_prologues(pre, iters):
     """The fused prologue on the 3.8B-shaped prefill batch, plain and with QK
     normalisation (HBM-bound: q, k, v read once; q and the cache rows written
@@ -403,6 +442,7 @@ def main():
     }
     result["diff_attn"] = Diff(rgc, synth).time(max(args.steps, 5))
     result["prologue"] = time_prologues(pre, max(args.steps, 5))
+    result["varlen_prefill"] = Varlen(rgc, synth).time(max(args.steps, 5))
     print("[bench] timed the differential attention", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -191,6 +191,31 @@ int rgc_gqa_attn_prefill(void* o, const void* q, const void* k_cache,
                          float* lse, int32_t* err_flag, void* stream);
 
 /*
+ * rgc_gqa_attn_prefill_varlen -- causal GQA over packed documents: several
+ * token sequences laid end to end, each token attending only to the tokens
+ * of its own document at or before it (document masking with per-token
+ * document ids: page "训练3.8B LLM至0.384 CORE，成本998美元 – Hugo Vergnes",
+ * section 无效的方法).
+ *   q, o       [T,Hq,D] bf16, strides (q_ts, q_hs) / (o_ts, o_hs); T =
+ *              total_tokens.  o is written for every token of every document.
+ *   k, v       [T,Hkv,D] bf16, both with strides (kv_ts, kv_hs): the packed,
+ *              already rotated keys and values of the same tokens.
+ *   cu_seqlens [n_docs + 1] int32, device: document i is tokens
+ *              cu_seqlens[i] .. cu_seqlens[i+1]-1 (non-decreasing, from 0 to
+ *              at most T).
+ *   max_seqlen host: the longest document (sizes the launch).
+ *   lse        [Hq,T] fp32 or NULL.
+ * bf16 only; head dim 32, 64 or 128.  Offsets that are decreasing, exceed T
+ * or give a document longer than max_seqlen raise *err_flag and that
+ * document is not computed.  Same arithmetic as rgc_gqa_attn_prefill.
+ */
+int rgc_gqa_attn_prefill_varlen(void* o, const void* q, const void* k, const void* v, int dtype, int n_docs,
+                                const int32_t* cu_seqlens, int max_seqlen, int total_tokens, int Hq,
+                                int Hkv, int D, int64_t q_ts, int64_t q_hs, int64_t o_ts, int64_t o_hs,
+                                int64_t kv_ts, int64_t kv_hs, float scale, float* lse, int32_t* err_flag,
+                                void* stream);
+
+/*
  * rgc_diff_attn_prefill -- causal differential attention with grouped KV
  * heads (page "750美元从零训练3个LLM：一位开发者的实战复盘", section
  * "V2：引入前沿技术": a second attention map, weighted by lambda, is

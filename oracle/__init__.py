@@ -174,6 +174,32 @@ def attn(q, k_cache, v_cache, q_start=None, scale=None, want_lse=False, nthreads
     return (o, lse) if want_lse else o
 
 
+def attn_varlen(q, k, v, cu_seqlens, scale=None, want_lse=False, nthreads=None):
+    """Causal GQA over packed documents (document masking, page "训练3.8B LLM至
+    0.384 CORE，成本998美元 – Hugo Vergnes", section 无效的方法): q [T,Hq,D],
+    k, v [T,Hkv,D]; document i is tokens cu_seqlens[i]..cu_seqlens[i+1]-1 and
+    each of its tokens attends to its own document's tokens at or before it.
+    Each document is one orc_attn call on its slice.  Returns float64 o
+    [T,Hq,D] (and lse [Hq,T])."""
+    q, k, v = map(_cpu, (q, k, v))
+    T, Hq, D = q.shape
+    cu = [int(c) for c in _cpu(cu_seqlens).tolist()]
+    o = torch.empty((T, Hq, D), dtype=torch.float64)
+    lse = torch.empty((Hq, T), dtype=torch.float64) if want_lse else None
+    for c0, c1 in zip(cu[:-1], cu[1:]):
+        if c1 == c0:
+            continue
+        # document slice as a batch of one: q [1,n,Hq,D], k/v as a [1,Hkv,n,D] cache view
+        r = attn(q[c0:c1][None], k[c0:c1].transpose(0, 1)[None], v[c0:c1].transpose(0, 1)[None],
+                 None, scale, want_lse, nthreads)
+        if want_lse:
+            o[c0:c1] = r[0][0]
+            lse[:, c0:c1] = r[1][0]
+        else:
+            o[c0:c1] = r[0]
+    return (o, lse) if want_lse else o
+
+
 def attn_decode(q, k_cache, v_cache, seq_lens, scale=None, want_lse=False, nthreads=None):
     """Cached decode of q [B,Hq,D] at slot seq_lens[b]-1; float64 o [B,Hq,D]."""
     q, k_cache, v_cache = map(_cpu, (q, k_cache, v_cache))

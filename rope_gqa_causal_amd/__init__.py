@@ -24,6 +24,7 @@ __all__ = [
     "RgcError", "library", "rope_apply", "kv_cache_append", "rope_append", "norm_rope_append",
     "gqa_attn_prefill",
     "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace", "diff_attn_prefill",
+    "gqa_attn_prefill_varlen",
     "ROPE_HALF", "ROPE_INTERLEAVED",
 ]
 
@@ -52,6 +53,8 @@ _SIGNATURES = {
     "rgc_gqa_attn_prefill": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
                                   _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _p, _f, _p, _p, _p]),
+    "rgc_gqa_attn_prefill_varlen": (_i, [_p, _p, _p, _p, _i, _i, _p, _i, _i, _i, _i, _i,
+                                         _i64, _i64, _i64, _i64, _i64, _i64, _f, _p, _p, _p]),
     "rgc_diff_attn_prefill": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
                                    _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                    _p, _f, _f, _p, _p]),
@@ -205,6 +208,29 @@ def gqa_attn_prefill(q, k_cache, v_cache, q_start=None, scale=None, out=None, ls
           o.stride(0), o.stride(1), o.stride(2),
           k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
           _ptr(q_start), float(scale), _ptr(lse), _ptr(err_flag), _stream(q))
+    return o
+
+
+def gqa_attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, out=None, lse=None, err_flag=None):
+    """Causal GQA over packed documents: q [T,Hq,D], k, v [T,Hkv,D] (bf16);
+    document i is tokens cu_seqlens[i]..cu_seqlens[i+1]-1 and attends only to
+    itself.  max_seqlen (host int) bounds every document's length."""
+    _gpu(q, k, v, cu_seqlens, out, lse, err_flag)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (T, Hkv, D) or v.shape != k.shape or v.stride() != k.stride():
+        raise ValueError("k and v must be [T,Hkv,D] with the same strides")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous() or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a contiguous int32 vector")
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q) if out is None else out
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (Hq, T)):
+        raise ValueError("lse must be a contiguous float32 [Hq,T] tensor")
+    _call("rgc_gqa_attn_prefill_varlen", _ptr(o), _ptr(q), _ptr(k), _ptr(v), _dtype(q),
+          cu_seqlens.numel() - 1, _ptr(cu_seqlens), int(max_seqlen), T, Hq, Hkv, D,
+          q.stride(0), q.stride(1), o.stride(0), o.stride(1), k.stride(0), k.stride(1),
+          float(scale), _ptr(lse), _ptr(err_flag), _stream(q))
     return o
 
 

@@ -241,6 +241,52 @@ int rgc_gqa_attn_prefill(void* o, const void* q, const void* k_cache, const void
   return hip_status(dtype == RGC_BF16 ? launch_prefill_bf16(p, s) : launch_attn_f32(p, false, s));
 }
 
+int rgc_gqa_attn_prefill_varlen(void* o, const void* q, const void* k, const void* v, int dtype, int n_docs,
+                                const int32_t* cu_seqlens, int max_seqlen, int total_tokens, int Hq, int Hkv,
+                                int D, int64_t q_ts, int64_t q_hs, int64_t o_ts, int64_t o_hs, int64_t kv_ts,
+                                int64_t kv_hs, float scale, float* lse, int32_t* err_flag, void* stream) {
+  int st = check_attn_common(dtype, n_docs, max_seqlen, Hq, Hkv, D, total_tokens);
+  if (st != RGC_OK) return st;
+  if (dtype != RGC_BF16) return RGC_ERR_DTYPE;
+  if (n_docs == 0 || max_seqlen == 0 || total_tokens == 0) return RGC_OK;
+  if (!o || !q || !k || !v || !cu_seqlens) return RGC_ERR_NULL;
+  if (max_seqlen > total_tokens) return RGC_ERR_CAPACITY;
+  if (!std::isfinite(scale)) return RGC_ERR_ARG;
+  if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return RGC_ERR_LAYOUT;
+  if (!stride_ok(q_ts, dtype) || !stride_ok(q_hs, dtype) || !stride_ok(o_ts, dtype) || !stride_ok(o_hs, dtype) ||
+      !stride_ok(kv_ts, dtype) || !stride_ok(kv_hs, dtype))
+    return RGC_ERR_LAYOUT;
+  if ((int64_t)n_docs * Hq * ((max_seqlen + 255) / 256) > 0x7FFFFFFFLL) return RGC_ERR_SHAPE;
+  AttnParams p = {};
+  p.o = o;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.B = n_docs;
+  p.Sq = max_seqlen;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.S_max = total_tokens;
+  p.q_sb = 0;
+  p.q_ss = q_ts;
+  p.q_sh = q_hs;
+  p.o_sb = 0;
+  p.o_ss = o_ts;
+  p.o_sh = o_hs;
+  p.kv_sb = 0;
+  p.kv_sh = kv_hs;
+  p.kv_ss = kv_ts;
+  p.q_start = nullptr;
+  p.cu_seqlens = cu_seqlens;
+  p.seq_lens = nullptr;
+  p.max_len = total_tokens;
+  p.scale = scale;
+  p.lse = lse;
+  p.err = err_flag;
+  return hip_status(launch_prefill_bf16(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2, const void* k1_cache,
                           const void* k2_cache, const void* v_cache, int dtype, int B, int Sq, int Hq,
                           int Hkv, int D, int S_max, int64_t q_sb, int64_t q_ss, int64_t q_sh,

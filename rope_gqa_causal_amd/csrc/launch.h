@@ -67,6 +67,7 @@ struct AttnParams {
   int64_t o_sb, o_ss, o_sh;
   int64_t kv_sb, kv_sh, kv_ss;
   const int32_t* q_start;   // prefill
+  const int32_t* cu_seqlens;  // packed-document prefill: [B + 1] token offsets (else NULL)
   const int32_t* seq_lens;  // decode
   int max_len;              // decode: host bound on seq_lens
   float scale;

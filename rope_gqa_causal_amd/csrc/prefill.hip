@@ -250,49 +250,85 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
   constexpr int KS = T::KS, DB = T::DB;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
-  // XCD-aware order.  Workgroup i runs on XCD i % 8; relabel so that each
-  // XCD walks a contiguous range of (sequence, KV head) groups, and within a
-  // group all its query heads and q-tiles, heaviest q-tile first.  The
-  // workgroups resident on one XCD then share one or two groups' K/V in
+  // XCD-aware order.  Workgroup i runs on XCD i % 8.  Units u = (sequence,
+  // KV head) stay on one XCD, so the query heads of a unit share its K/V in
   // that XCD's L2.
+  //  * Padded batch: each XCD walks a contiguous range of units, and within a
+  //    unit all its query heads and q-tiles, heaviest q-tile first.
+  //  * Packed documents (lengths differ widely): XCD x takes the units u = x
+  //    (mod 8) and walks them q-tile slab by q-tile slab, heaviest slab first
+  //    across all documents, so the long documents' heavy tiles start at once.
   const int group = p.Hq / p.Hkv;
-  const int per_group = group * nqt;
-  const int total = p.B * p.Hkv * per_group;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int lid = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (lid >= total) return;
-  const int gidx = lid / per_group;      // (b, kvh)
-  const int widx = lid % per_group;
-  const int qt = nqt - 1 - widx / group;  // heaviest tiles first
-  const int kvh = gidx % p.Hkv;
-  const int b = gidx / p.Hkv;
-  const int h = kvh * group + widx % group;
+  int qt, b, kvh, h;
+  if (!p.cu_seqlens) {
+    const int per_group = group * nqt;
+    const int total = p.B * p.Hkv * per_group;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int lid = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (lid >= total) return;
+    const int gidx = lid / per_group;      // (b, kvh)
+    const int widx = lid % per_group;
+    qt = nqt - 1 - widx / group;            // heaviest tiles first
+    kvh = gidx % p.Hkv;
+    b = gidx / p.Hkv;
+    h = kvh * group + widx % group;
+  } else {
+    const int units = p.B * p.Hkv;
+    const int x = (int)(blockIdx.x % kXcds), r = (int)(blockIdx.x / kXcds);
+    const int cnt = x < units ? (units - x + kXcds - 1) / kXcds : 0;  // units u = x (mod 8)
+    const int per_slab = cnt * group;
+    if (r >= per_slab * nqt) return;
+    const int within = r % per_slab;
+    qt = nqt - 1 - r / per_slab;
+    const int u = x + kXcds * (within / group);
+    kvh = u % p.Hkv;
+    b = u / p.Hkv;
+    h = kvh * group + within % group;
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
 
-  const int first = p.q_start ? p.q_start[b] : 0;
+  // Rows of this sequence.  Padded batch: row s of sequence b sits at slot
+  // q_start[b] + s of cache row b.  Packed documents (cu_seqlens): document b
+  // is tokens cu[b] .. cu[b+1]-1 of q, o and the packed k, v, and its row s
+  // sees its own tokens 0..s only.
+  int Sq = p.Sq, first = p.q_start ? p.q_start[b] : 0;  // packed: p.Sq bounds every document
+  int64_t tok0 = 0;
+  if (p.cu_seqlens) {
+    tok0 = p.cu_seqlens[b];
+    Sq = p.cu_seqlens[b + 1] - (int)tok0;
+    first = 0;
+    if (tok0 < 0 || Sq < 0 || Sq > p.Sq || tok0 + Sq > p.S_max) {  // malformed offsets: flag, touch nothing
+      if (tid == 0 && p.err) p.err[0] = 1;
+      return;
+    }
+    if (qt * kBM >= Sq) return;  // past this document's rows
+  }
   const int s_base = qt * kBM + wave * 32;  // this wave's first row
-  if (first < 0 || (int64_t)first + p.Sq > p.S_max) {
+  const int64_t q_row0 = (int64_t)b * p.q_sb + tok0 * p.q_ss + (int64_t)h * p.q_sh;
+  const int64_t o_row0 = (int64_t)b * p.o_sb + tok0 * p.o_ss + (int64_t)h * p.o_sh;
+  const int64_t lse_row0 = p.cu_seqlens ? (int64_t)h * p.S_max + tok0 : ((int64_t)b * p.Hq + h) * Sq;
+  if (first < 0 || (int64_t)first + Sq > p.S_max) {
     // Device-side capacity violation: NaN rows, flag, no cache access.
-    if (s_base + col < p.Sq && half == 0) {
-      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb +
-                     (int64_t)(s_base + col) * p.o_ss + (int64_t)h * p.o_sh;
+    if (s_base + col < Sq && half == 0) {
+      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + o_row0 + (int64_t)(s_base + col) * p.o_ss;
       for (int d = 0; d < D; ++d) orow[d] = 0x7FC0;
-      if (p.lse) p.lse[((int64_t)b * p.Hq + h) * p.Sq + s_base + col] = __builtin_nanf("");
+      if (p.lse) p.lse[lse_row0 + s_base + col] = __builtin_nanf("");
     }
     if (tid == 0 && p.err) p.err[0] = 1;
     return;
   }
 
-  const int s_end_wg = min(p.Sq, (qt + 1) * kBM);     // rows [qt*kBM, s_end_wg)
+  const int s_end_wg = min(Sq, (qt + 1) * kBM);       // rows [qt*kBM, s_end_wg)
   const int kmax = first + s_end_wg - 1;                // last key the workgroup needs
   const int nkt = kmax / kKT + 1;
-  const int wave_rows = min(32, p.Sq - s_base);         // <= 0: a wave past the ragged tail
+  const int wave_rows = min(32, Sq - s_base);           // <= 0: a wave past the ragged tail
   const int wave_last = wave_rows > 0 ? (first + s_base + wave_rows - 1) / kKT : -1;
   const int diag_from = (first + s_base) / kKT;         // first tile that needs the mask
 
-  const char* kb = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh) * 2;
-  const char* vb = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh) * 2;
+  const int64_t kv_off = ((int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh + tok0 * p.kv_ss) * 2;
+  const char* kb = reinterpret_cast<const char*>(p.k) + kv_off;
+  const char* vb = reinterpret_cast<const char*>(p.v) + kv_off;
 
   WaveCtx<D> w;
   w.c = p.scale * kLog2e;
@@ -300,11 +336,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
   {
     // Q^T fragments: lane holds query `col`, d = 16*ks + 8*half .. +8.
     const int s = s_base + col;
-    const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb +
-                       (int64_t)s * p.q_ss + (int64_t)h * p.q_sh;
+    const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + q_row0 + (int64_t)s * p.q_ss;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      w.qf[ks] = (s < p.Sq) ? ld16(qr + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
+      w.qf[ks] = (s < Sq) ? ld16(qr + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
   }
   // K fragment: row `col` (block 1 is 32 rows further) at logical chunk
   // 2ks + half.  V^T fragment for d-block q: rows 4half + x/4 (+16kk, +8),
@@ -353,10 +388,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
   if (wave_last >= 0) {
     const float lsum = sum_halves(w.l_run);
     const int s = s_base + col;
-    if (s < p.Sq) {
+    if (s < Sq) {
       const float inv = 1.f / lsum;
-      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)s * p.o_ss +
-                     (int64_t)h * p.o_sh;
+      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + o_row0 + (int64_t)s * p.o_ss;
 #pragma unroll
       for (int q = 0; q < DB; ++q)
 #pragma unroll
@@ -367,8 +401,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
           wv[1] = pack_bf16x2(w.acc_o[q][4 * q4 + 2] * inv, w.acc_o[q][4 * q4 + 3] * inv);
           *reinterpret_cast<u32x2*>(orow + d) = wv;
         }
-      if (p.lse && half == 0)
-        p.lse[((int64_t)b * p.Hq + h) * p.Sq + s] = (w.m_run + log2f(lsum)) * kLn2;
+      if (p.lse && half == 0) p.lse[lse_row0 + s] = (w.m_run + log2f(lsum)) * kLn2;
     }
   }
 }
@@ -376,7 +409,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
 template <int D>
 hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   const int nqt = (p.Sq + kBM - 1) / kBM;
-  const int total = p.B * p.Hq * nqt;
+  int64_t total = (int64_t)p.B * p.Hq * nqt;
+  if (p.cu_seqlens)  // every XCD sized for the largest unit share
+    total = (int64_t)kXcds * ((p.B * p.Hkv + kXcds - 1) / kXcds) * (p.Hq / p.Hkv) * nqt;
   const dim3 grid((unsigned)(((total + kXcds - 1) / kXcds) * kXcds));
   hipLaunchKernelGGL(prefill_kernel<D>, grid, dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream, p, nqt);
   return hipGetLastError();

@@ -23,6 +23,10 @@ Workload shapes and where they come from:
   token per sequence.
 * ``diff``: differential attention, batch 4, 1024 tokens, 16 query / 8 KV
   heads, two maps of dim 64, value dim 64, lambda 0.8, bf16.
+* ``varlen``: the 3.8B-shaped prefill's 16384 tokens packed as documents
+  whose lengths are uniform on {64..4096} (the last one cut to fit), 24 query
+  / 8 KV heads of dim 128, bf16: document-masked packing as on the 3.8B page
+  (section 无效的方法).
 """
 from dataclasses import dataclass, field
 
@@ -64,7 +68,21 @@ WORKLOADS = {
                               steps=32, len_lo=256, len_hi=2048, seed=4),
     "diff": Workload("diff", B=4, Hq=16, Hkv=8, D=64, dtype=torch.bfloat16, S=1024,
                      Dv=64, lam=0.8, seed=5),
+    "varlen": Workload("varlen", B=1, Hq=24, Hkv=8, D=128, dtype=torch.bfloat16, S=16384,
+                       len_lo=64, len_hi=4096, seed=6),
 }
+
+
+def document_lengths(total: int, lo: int, hi: int, gen: torch.Generator) -> torch.Tensor:
+    """Document lengths uniform on {lo..hi} drawn until they cover ``total``
+    tokens; the last one is cut so the lengths sum to ``total`` (int32)."""
+    out, used = [], 0
+    while used < total:
+        n = int(torch.randint(lo, hi + 1, (1,), generator=gen).item())
+        n = min(n, total - used)
+        out.append(n)
+        used += n
+    return torch.tensor(out, dtype=torch.int32)
 
 
 def generator(seed: int) -> torch.Generator:

@@ -29,7 +29,7 @@ def test_header_symbols_are_exported():
     assert {"rgc_rope_apply", "rgc_kv_cache_append", "rgc_rope_append", "rgc_norm_rope_append",
             "rgc_gqa_attn_prefill",
             "rgc_gqa_attn_decode", "rgc_gqa_attn_decode_workspace_size",
-            "rgc_diff_attn_prefill"} <= set(names)
+            "rgc_diff_attn_prefill", "rgc_gqa_attn_prefill_varlen"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -89,6 +89,26 @@ def test_diff_rejects_bad_arguments_before_launch():
     assert _diff(lam=float("inf")) == -10
     assert _diff(B=0) == OK
     assert _diff(Sq=0) == OK
+
+
+def _varlen(**kw):
+    a = dict(o=A, q=A, k=A, v=A, dt=BF16, n=3, cu=A, maxlen=16, T=40, Hq=4, Hkv=2, D=64, q_ts=256, q_hs=64,
+             o_ts=256, o_hs=64, kv_ts=128, kv_hs=64, scale=0.125, lse=None, err=None)
+    a.update(kw)
+    return rgc.library().rgc_gqa_attn_prefill_varlen(
+        a["o"], a["q"], a["k"], a["v"], a["dt"], a["n"], a["cu"], a["maxlen"], a["T"], a["Hq"], a["Hkv"], a["D"],
+        a["q_ts"], a["q_hs"], a["o_ts"], a["o_hs"], a["kv_ts"], a["kv_hs"], a["scale"], a["lse"], a["err"], None)
+
+
+def test_varlen_rejects_bad_arguments_before_launch():
+    assert _varlen(Hq=3) == GROUP
+    assert _varlen(dt=F32) == DTYPE
+    assert _varlen(D=96) == HEADDIM
+    assert _varlen(cu=None) == NULL
+    assert _varlen(maxlen=41) == CAPACITY
+    assert _varlen(kv_ts=127) == LAYOUT
+    assert _varlen(n=0) == OK
+    assert _varlen(T=0, maxlen=0) == OK
 
 
 def _decode(**kw):
