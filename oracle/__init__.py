@@ -36,6 +36,11 @@ def _load():
                                      _c_i64, _c_i64, _c_i64, _c_p, _c_d, _c_int]
         lib.orc_norm_rope_f64.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                           _c_i64, _c_i64, _c_i64, _c_p, _c_d, _c_int, _c_d]
+        lib.orc_rope_grad_f64.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                          _c_i64, _c_i64, _c_i64, _c_p, _c_d, _c_int]
+        lib.orc_attn_backward.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int,
+                                          _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_i64,
+                                          _c_i64, _c_i64, _c_i64, _c_d, _c_int]
         lib.orc_rope_apply.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_i64, _c_i64, _c_i64, _c_p, _c_d, _c_int]
         lib.orc_kv_cache_append.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -198,6 +203,36 @@ def attn_varlen(q, k, v, cu_seqlens, scale=None, want_lse=False, nthreads=None):
         else:
             o[c0:c1] = r[0]
     return (o, lse) if want_lse else o
+
+
+def attn_backward(q, k, v, dO, scale=None, nthreads=None):
+    """Gradients of causal GQA self-attention: q, dO [B,S,Hq,D] (same
+    strides), k, v [B,S,Hkv,D] (same strides).  Returns float64 dq, dk, dv."""
+    q, k, v, dO = map(_cpu, (q, k, v, dO))
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert tuple(dO.stride()) == tuple(q.stride()) and tuple(v.stride()) == tuple(k.stride())
+    if scale is None:
+        scale = D ** -0.5
+    dq = torch.empty((B, S, Hq, D), dtype=torch.float64)
+    dk = torch.empty((B, S, Hkv, D), dtype=torch.float64)
+    dv = torch.empty((B, S, Hkv, D), dtype=torch.float64)
+    _check(_load().orc_attn_backward(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), dO.data_ptr(), _dt(q), B, S, Hq, Hkv, D,
+                                     q.stride(0), q.stride(1), q.stride(2), k.stride(0), k.stride(1),
+                                     k.stride(2), float(scale), _threads(nthreads)))
+    return dq, dk, dv
+
+
+def rope_grad_f64(g, pos0=None, base=10000.0, style=ROPE_HALF):
+    """Gradient through RoPE (g [B,S,H,D] turned back by its angle); float64."""
+    g = _cpu(g)
+    B, S, H, D = g.shape
+    out = torch.empty((B, S, H, D), dtype=torch.float64)
+    p, pp = _i32(pos0, B)
+    _check(_load().orc_rope_grad_f64(out.data_ptr(), g.data_ptr(), _dt(g), B, S, H, D,
+                                     g.stride(0), g.stride(1), g.stride(2), pp, base, style))
+    return out
 
 
 def attn_decode(q, k_cache, v_cache, seq_lens, scale=None, want_lse=False, nthreads=None):

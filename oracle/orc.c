@@ -122,6 +122,36 @@ int orc_rope_apply(void* x, int dt, int B, int S, int H, int D, int64_t sb,
   return ORC_OK;
 }
 
+/*
+ * Gradient through RoPE: the rotation is orthogonal, so the gradient with
+ * respect to the unrotated vector is the output gradient turned back by the
+ * same angle: (ga, gb) -> (ga cos + gb sin, -ga sin + gb cos).
+ */
+int orc_rope_grad_f64(double* out, const void* g, int dt, int B, int S, int H,
+                      int D, int64_t sb, int64_t ss, int64_t sh,
+                      const int32_t* pos0, double base, int style) {
+  if (!rope_args_ok(dt, B, S, H, D, style)) return ORC_ERR_ARG;
+  int half = D / 2;
+  for (int b = 0; b < B; ++b)
+    for (int s = 0; s < S; ++s) {
+      double pos = (double)((pos0 ? pos0[b] : 0) + s);
+      for (int h = 0; h < H; ++h) {
+        int64_t off = (int64_t)b * sb + (int64_t)s * ss + (int64_t)h * sh;
+        double* dst = out + (((int64_t)b * S + s) * H + h) * D;
+        for (int i = 0; i < half; ++i) {
+          double theta = pow(base, -2.0 * (double)i / (double)D);
+          double c = cos(pos * theta), sn = sin(pos * theta);
+          int ia = (style == ORC_ROPE_HALF) ? i : 2 * i;
+          int ib = (style == ORC_ROPE_HALF) ? i + half : 2 * i + 1;
+          double ga = load(g, dt, off + ia), gb = load(g, dt, off + ib);
+          dst[ia] = ga * c + gb * sn;
+          dst[ib] = -ga * sn + gb * c;
+        }
+      }
+    }
+  return ORC_OK;
+}
+
 /* ---- QK normalisation before RoPE ----------------------------------------- */
 
 /*
@@ -284,6 +314,76 @@ int orc_attn(double* o, double* lse, const void* q, const void* k_cache,
       if (lse) lse[((int64_t)b * Hq + h) * Sq + s] = m + log(l);
     }
     free(w);
+  }
+  return ORC_OK;
+}
+
+/*
+ * Gradients of causal GQA self-attention (the training pass: the pages train
+ * the 24 q / 8 KV model of [P3] 设置 end to end).  For row i of query head h
+ * (keys j <= i of the same sequence, KV head h / group) with softmax weights
+ * w_ij, and the output gradient dO_i:
+ *   dV_j += w_ij dO_i              (summed over the group's query heads)
+ *   dP_ij = dO_i . V_j,   Dlt_i = sum_j w_ij dP_ij
+ *   dS_ij = w_ij (dP_ij - Dlt_i)
+ *   dQ_i  = scale sum_j dS_ij K_j
+ *   dK_j += scale dS_ij Q_i        (summed over the group's query heads)
+ * q and dO share one layout [B,S,Hq,D]; k and v [B,S,Hkv,D].  dq, dk, dv are
+ * contiguous doubles of the same shapes.  OpenMP over (sequence, KV head)
+ * units, so each dk/dv row is written by one thread.
+ */
+int orc_attn_backward(double* dq, double* dk, double* dv, const void* q,
+                      const void* k, const void* v, const void* dO, int dt,
+                      int B, int S, int Hq, int Hkv, int D, int64_t q_sb,
+                      int64_t q_ss, int64_t q_sh, int64_t kv_sb, int64_t kv_ss,
+                      int64_t kv_sh, double scale, int nthreads) {
+  if (!attn_args_ok(dt, B, S, Hq, Hkv, D, S)) return ORC_ERR_ARG;
+  if (Hq % Hkv != 0) return ORC_ERR_GROUP;
+  const int group = Hq / Hkv;
+  const int64_t units = (int64_t)B * Hkv;
+  if (nthreads < 1) nthreads = 1;
+  for (int64_t i = 0; i < (int64_t)B * S * Hkv * D; ++i) dk[i] = dv[i] = 0.0;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+      int b = (int)(u / Hkv), kvh = (int)(u % Hkv);
+      int64_t kv_off = (int64_t)b * kv_sb + (int64_t)kvh * kv_sh;
+      for (int hh = 0; hh < group; ++hh) {
+        int h = kvh * group + hh;
+        for (int i = 0; i < S; ++i) {
+          int64_t q_off = (int64_t)b * q_sb + (int64_t)i * q_ss + (int64_t)h * q_sh;
+          double m;
+          double l = row_weights(w, q, q_off, k, kv_off, kv_ss, dt, D, i, scale, &m);
+          double dlt = 0.0;
+          for (int j = 0; j <= i; ++j) {
+            w[j] /= l;
+            double acc = 0.0;
+            int64_t vr = kv_off + (int64_t)j * kv_ss;
+            for (int d = 0; d < D; ++d) acc += load(dO, dt, q_off + d) * load(v, dt, vr + d);
+            dp[j] = acc;
+            dlt += w[j] * acc;
+          }
+          double* dqr = dq + (((int64_t)b * S + i) * Hq + h) * D;
+          for (int d = 0; d < D; ++d) dqr[d] = 0.0;
+          for (int j = 0; j <= i; ++j) {
+            double ds = w[j] * (dp[j] - dlt);
+            int64_t kr = kv_off + (int64_t)j * kv_ss;
+            double* dkr = dk + (((int64_t)b * S + j) * Hkv + kvh) * D;
+            double* dvr = dv + (((int64_t)b * S + j) * Hkv + kvh) * D;
+            for (int d = 0; d < D; ++d) {
+              dqr[d] += scale * ds * load(k, dt, kr + d);
+              dkr[d] += scale * ds * load(q, dt, q_off + d);
+              dvr[d] += w[j] * load(dO, dt, q_off + d);
+            }
+          }
+        }
+      }
+    }
+    free(w);
+    free(dp);
   }
   return ORC_OK;
 }

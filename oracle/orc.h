@@ -150,6 +150,26 @@ int orc_diff_attn(double* o, const void* q1, const void* q2, const void* k1,
                   const int32_t* q_start, double lambda,
                   double scale, int nthreads);
 
+/*
+ * Gradients of causal GQA self-attention for output gradient dO (same layout
+ * as q): dq [B,S,Hq,D], dk and dv [B,S,Hkv,D], contiguous doubles; dk and dv
+ * sum over the query heads of each group.  k, v [B,S,Hkv,D] with element
+ * strides (kv_sb, kv_ss, kv_sh).
+ */
+int orc_attn_backward(double* dq, double* dk, double* dv, const void* q,
+                      const void* k, const void* v, const void* dO, int dt,
+                      int B, int S, int Hq, int Hkv, int D, int64_t q_sb,
+                      int64_t q_ss, int64_t q_sh, int64_t kv_sb, int64_t kv_ss,
+                      int64_t kv_sh, double scale, int nthreads);
+
+/*
+ * Gradient through RoPE: g [B,S,H,D] (layout as orc_rope_f64) turned back by
+ * the angle of its position; out contiguous doubles.
+ */
+int orc_rope_grad_f64(double* out, const void* g, int dt, int B, int S, int H,
+                      int D, int64_t sb, int64_t ss, int64_t sh,
+                      const int32_t* pos0, double base, int style);
+
 #ifdef __cplusplus
 }
 #endif
