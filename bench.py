@@ -14,8 +14,9 @@ reported beside it (TFLOP/s over unmasked query-key pairs).  Both are also
 given per kernel against the MI355X peaks (HBM 8 TB/s; dense bf16 MFMA
 2.5 PFLOP/s), from HIP events recorded on the stream the kernels run on.
 The differential-attention variant (`diff_attn`), the packed-document prefill
-(`varlen_prefill`) and the fused prologue with and without QK normalisation
-(`prologue`) are timed apart on their own workloads.  The fp64 CPU oracle is timed on a bounded sample of the same
+(`varlen_prefill`), the fused prologue with and without QK normalisation
+(`prologue`) and the attention backward (`backward`) are timed apart on their
+own workloads.  The fp64 CPU oracle is timed on a bounded sample of the same
 decode workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -274,6 +275,36 @@ class Varlen:
                 "workload": "16384 tokens packed as documents of U{64..4096} tokens, 24q/8kv, D128, bf16"}
 
 
+def time_backward(rgc, synth, iters):
+    """Attention backward (dq, dk, dv) on the 3.8B-shaped batch (B 8 x 2048,
+    24 q / 8 KV, D 128), from the forward's output and lse."""
+    w = synth.WORKLOADS["prefill3p8b"]
+    g = synth.generator(w.seed + 100)
+    q, k, v = (t.cuda() for t in synth.qkv(w.B, w.S, w.Hq, w.Hkv, w.D, g, w.dtype))
+    d_o = synth.normal((w.B, w.S, w.Hq, w.D), g, w.dtype).cuda()
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda")
+    o = rgc.gqa_attn_prefill(q, k.transpose(1, 2), v.transpose(1, 2), lse=lse)
+    ws = rgc.backward_workspace(w.B, w.S, w.Hq)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    run = lambda: rgc.gqa_attn_backward(q, k, v, o, d_o, lse, workspace=ws, dq=dq, dk=dk, dv=dv)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / iters * 1e3
+    flops = 10.0 * w.D * w.B * w.Hq * w.S * (w.S + 1) / 2  # five products per unmasked pair x 2D
+    tf = flops / (us * 1e-6) / 1e12
+    return {"bound": "mfma", "kernel": "gqa_attn_backward (delta + dK/dV + dQ)", "achieved": round(tf, 2),
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_launch": flops, "avg_launch_us": round(us, 3),
+            "workload": "B8 x 2048, 24q/8kv, D128, bf16; FLOPs count S, dP, dV, dK, dQ (2D each) per unmasked pair"}
+
+
 def time_prologues(pre, iters):
     """The fused prologue on the 3.8B-shaped prefill batch, plain and with QK
     normalisation (HBM-bound: q, k, v read once; q and the cache rows written
@@ -443,6 +474,7 @@ def main():
     result["diff_attn"] = Diff(rgc, synth).time(max(args.steps, 5))
     result["prologue"] = time_prologues(pre, max(args.steps, 5))
     result["varlen_prefill"] = Varlen(rgc, synth).time(max(args.steps, 5))
+    result["backward"] = time_backward(rgc, synth, max(args.steps, 3))
     print("[bench] timed the differential attention", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

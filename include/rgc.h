@@ -102,6 +102,15 @@ int rgc_rope_apply(void* x, int dtype, int B, int S, int H, int D, int64_t sb,
                    int style, void* stream);
 
 /*
+ * rgc_rope_backward -- the gradient through RoPE: g [B,S,H,D] (layout as for
+ * rgc_rope_apply) is turned back, in place, by the angle of its position.
+ * The rotation is orthogonal, so this is exactly the gradient with respect
+ * to the unrotated vector.  Arguments and errors as for rgc_rope_apply.
+ */
+int rgc_rope_backward(void* g, int dtype, int B, int S, int H, int D, int64_t sb, int64_t ss, int64_t sh,
+                      const int32_t* pos0, double base, int style, void* stream);
+
+/*
  * rgc_kv_cache_append -- copy new key and value rows into the caches.
  *   k_cache, v_cache  [B,Hkv,S_max,D] of dtype, strides (c_sb, c_sh, c_ss)
  *                     shared by both caches.
@@ -214,6 +223,34 @@ int rgc_gqa_attn_prefill_varlen(void* o, const void* q, const void* k, const voi
                                 int Hkv, int D, int64_t q_ts, int64_t q_hs, int64_t o_ts, int64_t o_hs,
                                 int64_t kv_ts, int64_t kv_hs, float scale, float* lse, int32_t* err_flag,
                                 void* stream);
+
+/*
+ * rgc_gqa_attn_backward -- gradients of causal GQA self-attention (the
+ * training pass of the attention the 3.8B page trains: page "训练3.8B LLM至
+ * 0.384 CORE，成本998美元 – Hugo Vergnes", section 设置).  Row i of head h
+ * attends to keys 0..i of its own sequence (no cache offset).
+ *   dq               [B,S,Hq,D] bf16, written; q, o, d_o share its strides
+ *                    (q_sb, q_ss, q_sh).
+ *   dk, dv           [B,S,Hkv,D] bf16, written (summed over each group's
+ *                    query heads); k, v share their strides (kv_sb, kv_ss,
+ *                    kv_sh).
+ *   q, k, v          the forward inputs (q and k already rotated).
+ *   o, d_o           the forward output and its gradient.
+ *   lse              [B,Hq,S] fp32: the forward's log-sum-exp
+ *                    (rgc_gqa_attn_prefill's lse output, natural log).
+ *   workspace        >= rgc_gqa_attn_backward_workspace_size bytes,
+ *                    256-byte aligned, caller-owned scratch.
+ * bf16 only (RGC_ERR_DTYPE); head dim 32, 64 or 128.  The weights are
+ * recomputed from lse; P and dS are rounded to bf16 for the matrix cores and
+ * accumulate in fp32.  For the gradient with respect to the unrotated q and
+ * k, apply rgc_rope_backward to dq and dk.
+ */
+size_t rgc_gqa_attn_backward_workspace_size(int B, int S, int Hq);
+int rgc_gqa_attn_backward(void* dq, void* dk, void* dv, const void* q, const void* k, const void* v,
+                          const void* o, const void* d_o, const float* lse, int dtype, int B, int S, int Hq,
+                          int Hkv, int D, int64_t q_sb, int64_t q_ss, int64_t q_sh, int64_t kv_sb,
+                          int64_t kv_ss, int64_t kv_sh, float scale, void* workspace, size_t ws_bytes,
+                          void* stream);
 
 /*
  * rgc_diff_attn_prefill -- causal differential attention with grouped KV

@@ -24,7 +24,7 @@ __all__ = [
     "RgcError", "library", "rope_apply", "kv_cache_append", "rope_append", "norm_rope_append",
     "gqa_attn_prefill",
     "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace", "diff_attn_prefill",
-    "gqa_attn_prefill_varlen",
+    "gqa_attn_prefill_varlen", "rope_backward", "gqa_attn_backward", "backward_workspace",
     "ROPE_HALF", "ROPE_INTERLEAVED",
 ]
 
@@ -44,6 +44,10 @@ _SIGNATURES = {
     "rgc_abi_version": (_i, []),
     "rgc_status_string": (ctypes.c_char_p, [_i]),
     "rgc_rope_apply": (_i, [_p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _d, _i, _p]),
+    "rgc_rope_backward": (_i, [_p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _d, _i, _p]),
+    "rgc_gqa_attn_backward_workspace_size": (_sz, [_i, _i, _i]),
+    "rgc_gqa_attn_backward": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                   _i64, _i64, _i64, _i64, _i64, _i64, _f, _p, _sz, _p]),
     "rgc_kv_cache_append": (_i, [_p, _p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _p, _i,
                                  _i64, _i64, _i64, _p, _p, _p]),
     "rgc_rope_append": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64,
@@ -139,6 +143,16 @@ def rope_apply(x, pos0=None, base=10000.0, style=ROPE_HALF):
     return x
 
 
+def rope_backward(g, pos0=None, base=10000.0, style=ROPE_HALF):
+    """Gradient through RoPE: turn g [B,S,H,D] back by its angles, in place."""
+    _gpu(g, pos0)
+    B, S, H, D = g.shape
+    pos0 = _lens(pos0, B, "pos0")
+    _call("rgc_rope_backward", _ptr(g), _dtype(g), B, S, H, D, g.stride(0), g.stride(1), g.stride(2),
+          _ptr(pos0), float(base), int(style), _stream(g))
+    return g
+
+
 def kv_cache_append(k_cache, v_cache, k_new, v_new, pos0, err_flag=None):
     """Copy k_new, v_new [B,S_new,Hkv,D] to slots pos0[b].. of caches [B,Hkv,S_max,D]."""
     _gpu(k_cache, v_cache, k_new, v_new, pos0, err_flag)
@@ -232,6 +246,38 @@ def gqa_attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None, out=Non
           q.stride(0), q.stride(1), o.stride(0), o.stride(1), k.stride(0), k.stride(1),
           float(scale), _ptr(lse), _ptr(err_flag), _stream(q))
     return o
+
+
+def backward_workspace(B, S, Hq, device="cuda"):
+    n = max(int(library().rgc_gqa_attn_backward_workspace_size(B, S, Hq)), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def gqa_attn_backward(q, k, v, o, d_o, lse, scale=None, workspace=None, dq=None, dk=None, dv=None):
+    """Gradients of causal GQA self-attention (bf16).  q, o, d_o [B,S,Hq,D]
+    (same strides); k, v [B,S,Hkv,D] (same strides); lse [B,Hq,S] fp32 from
+    gqa_attn_prefill.  Returns (dq, dk, dv)."""
+    _gpu(q, k, v, o, d_o, lse, workspace, dq, dk, dv)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if o.stride() != q.stride() or d_o.stride() != q.stride() or v.stride() != k.stride():
+        raise ValueError("q, o, d_o must share strides, and k, v")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, S):
+        raise ValueError("lse must be a contiguous float32 [B,Hq,S] tensor")
+    if scale is None:
+        scale = D ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != k.stride():
+        raise ValueError("gradients must have the strides of their inputs")
+    if workspace is None:
+        workspace = backward_workspace(B, S, Hq, q.device)
+    _call("rgc_gqa_attn_backward", _ptr(dq), _ptr(dk), _ptr(dv), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+          _ptr(d_o), _ptr(lse), _dtype(q), B, S, Hq, Hkv, D, q.stride(0), q.stride(1), q.stride(2),
+          k.stride(0), k.stride(1), k.stride(2), float(scale), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(q))
+    return dq, dk, dv
 
 
 def diff_attn_prefill(q1, q2, k1_cache, k2_cache, v_cache, lam, q_start=None, scale=None, out=None,

@@ -49,8 +49,10 @@ const char* rgc_status_string(int status) {
   }
 }
 
-int rgc_rope_apply(void* x, int dtype, int B, int S, int H, int D, int64_t sb, int64_t ss,
-                   int64_t sh, const int32_t* pos0, double base, int style, void* stream) {
+namespace {
+
+int rope_impl(void* x, int dtype, int B, int S, int H, int D, int64_t sb, int64_t ss, int64_t sh,
+              const int32_t* pos0, double base, int style, float sin_sign, void* stream) {
   if (!dtype_ok(dtype)) return RGC_ERR_DTYPE;
   if (B < 0 || S < 0 || H < 0 || D < 0) return RGC_ERR_SHAPE;
   if (D < 2 || D > kMaxRopeDim || D % 2 != 0) return RGC_ERR_HEADDIM;
@@ -69,9 +71,22 @@ int rgc_rope_apply(void* x, int dtype, int B, int S, int H, int D, int64_t sb, i
   p.ss = ss;
   p.sh = sh;
   p.pos0 = pos0;
+  p.sin_sign = sin_sign;
   for (int i = 0; i < kMaxRopeDim / 2; ++i)
     p.theta[i] = i < D / 2 ? std::pow(base, -2.0 * (double)i / (double)D) : 0.0;
   return hip_status(launch_rope(p, dtype, style, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int rgc_rope_apply(void* x, int dtype, int B, int S, int H, int D, int64_t sb, int64_t ss,
+                   int64_t sh, const int32_t* pos0, double base, int style, void* stream) {
+  return rope_impl(x, dtype, B, S, H, D, sb, ss, sh, pos0, base, style, 1.f, stream);
+}
+
+int rgc_rope_backward(void* g, int dtype, int B, int S, int H, int D, int64_t sb, int64_t ss,
+                      int64_t sh, const int32_t* pos0, double base, int style, void* stream) {
+  return rope_impl(g, dtype, B, S, H, D, sb, ss, sh, pos0, base, style, -1.f, stream);
 }
 
 int rgc_kv_cache_append(void* k_cache, void* v_cache, int dtype, int B, int Hkv, int D, int S_max,
@@ -285,6 +300,57 @@ int rgc_gqa_attn_prefill_varlen(void* o, const void* q, const void* k, const voi
   p.lse = lse;
   p.err = err_flag;
   return hip_status(launch_prefill_bf16(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t rgc_gqa_attn_backward_workspace_size(int B, int S, int Hq) {
+  if (B < 0 || S < 0 || Hq <= 0) return 0;
+  return backward_workspace_bytes(B, S, Hq);
+}
+
+int rgc_gqa_attn_backward(void* dq, void* dk, void* dv, const void* q, const void* k, const void* v,
+                          const void* o, const void* d_o, const float* lse, int dtype, int B, int S, int Hq,
+                          int Hkv, int D, int64_t q_sb, int64_t q_ss, int64_t q_sh, int64_t kv_sb,
+                          int64_t kv_ss, int64_t kv_sh, float scale, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  int st = check_attn_common(dtype, B, S, Hq, Hkv, D, S);
+  if (st != RGC_OK) return st;
+  if (dtype != RGC_BF16) return RGC_ERR_DTYPE;
+  if (B == 0 || S == 0) return RGC_OK;
+  if (!dq || !dk || !dv || !q || !k || !v || !o || !d_o || !lse) return RGC_ERR_NULL;
+  if (!std::isfinite(scale)) return RGC_ERR_ARG;
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(o) || !aligned16(d_o))
+    return RGC_ERR_LAYOUT;
+  if (!stride_ok(q_sb, dtype) || !stride_ok(q_ss, dtype) || !stride_ok(q_sh, dtype) ||
+      !stride_ok(kv_sb, dtype) || !stride_ok(kv_ss, dtype) || !stride_ok(kv_sh, dtype))
+    return RGC_ERR_LAYOUT;
+  if ((int64_t)B * S * Hq > 0x7FFFFFFFLL) return RGC_ERR_SHAPE;
+  const size_t need = backward_workspace_bytes(B, S, Hq);
+  if (!workspace || ws_bytes < need) return RGC_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RGC_ERR_LAYOUT;
+  BwdParams p = {};
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dO = d_o;
+  p.lse = lse;
+  p.B = B;
+  p.S = S;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.q_sb = q_sb;
+  p.q_ss = q_ss;
+  p.q_sh = q_sh;
+  p.kv_sb = kv_sb;
+  p.kv_ss = kv_ss;
+  p.kv_sh = kv_sh;
+  p.scale = scale;
+  return hip_status(launch_backward_bf16(p, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2, const void* k1_cache,

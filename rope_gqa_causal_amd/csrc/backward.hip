@@ -1,0 +1,387 @@
+// backward.hip -- gradients of causal GQA self-attention (bf16, MFMA).
+//
+// Operation: the training pass of the attention the pages run (the 24 q /
+// 8 KV model of page "训练3.8B LLM至0.384 CORE，成本998美元 – Hugo Vergnes",
+// section 设置, is trained end to end).  For row i of query head h with
+// weights w_ij = softmax_j(scale q_i.k_j) over keys j <= i and output
+// gradient dO_i:
+//   dV_j += w_ij dO_i,  dP_ij = dO_i . v_j,  dS_ij = w_ij (dP_ij - Dlt_i),
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j += scale dS_ij q_i,
+// where Dlt_i = sum_j w_ij dP_ij = dO_i . o_i, and dK, dV sum over the query
+// heads of each KV head's group.
+//
+// Three kernels, no atomics:
+//  * delta_kernel: Dlt_i = dO_i . o_i (fp32) per (sequence, head, row);
+//  * dkdv_kernel: a workgroup owns 128 keys of one (sequence, KV head) (32
+//    per wave, K and V in LDS) and walks every query head of the group and
+//    every query block of 32 rows at or after its keys: S = Q K^T and
+//    dP = dO V^T with keys in the MFMA N dimension, so each lane holds one
+//    key and P, dS are already the A operand of dV += P^T dO and
+//    dK += dS^T Q; dO and Q enter those as transposed fragments
+//    (ds_read_b64_tr_b16) of the row-major tiles;
+//  * dq_kernel: a workgroup owns 256 query rows of one (sequence, head) (32
+//    per wave) and walks the 64-key tiles at or before them: S^T = K Q^T and
+//    dP^T = V dO^T with queries in the N dimension (Q and dO fragments in
+//    registers), so dS^T is the B operand of dQ^T += K^T dS^T with K^T read
+//    transposed from the K tile.
+// The weights are recomputed from the forward pass's lse; P and dS are
+// rounded to bf16 for the MFMAs, everything accumulates in fp32, and dq, dk,
+// dv are rounded once to bf16.
+#include "common.h"
+#include "launch.h"
+#include "mfma_attn.h"
+
+namespace rgc {
+namespace {
+
+// Row-major bf16 tiles in LDS: 16-byte chunk c of row r sits at chunk
+// c ^ (r % CH), so 16-byte row fragments of 32 consecutive rows are
+// conflict-free.  Transposed fragments read the same layout through
+// per-lane addresses.
+template <int D>
+struct BTile {
+  static constexpr int CH = D / 8;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int ROW_BYTES = D * 2;
+  static __device__ __forceinline__ int phys(int r, int c) { return r * ROW_BYTES + 16 * (c ^ (r % CH)); }
+};
+
+// 16-byte row fragment: row r, logical chunk c.
+template <int D>
+__device__ __forceinline__ u32x4 row_frag(const char* tile, int r, int c) {
+  return *reinterpret_cast<const u32x4*>(tile + BTile<D>::phys(r, c));
+}
+
+// Transposed fragment of rows 16kk .. 16kk+15 and columns 32q .. 32q+31 of a
+// row-major tile: lane j gets, at column 32q + j%32, the values of rows
+// 16kk + 4h + (0..3) and 16kk + 8 + 4h + (0..3), h = j/32 -- the MFMA operand
+// layout whose k index runs over rows (see vt_frag).
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const char* tile, int q, int kk, int lane) {
+  const int x = lane & 15, beta = (lane >> 4) & 1, h = lane >> 5;
+  const int c_lane = 2 * beta + ((x & 3) >> 1);  // 4-column group inside the 32-column block
+  const int r = 16 * kk + 4 * h + (x >> 2);
+  const int c = 4 * q + c_lane;                   // logical 8-byte-pair chunk
+  const char* lo = tile + BTile<D>::phys(r, c) + 8 * (x & 1);
+  const char* hi = tile + BTile<D>::phys(r + 8, c) + 8 * (x & 1);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
+  const u32x2 a2 = __builtin_bit_cast(u32x2, a), b2 = __builtin_bit_cast(u32x2, b);
+  return u32x4{a2[0], a2[1], b2[0], b2[1]};
+}
+
+// Cooperative copy of `rows` rows (row stride `gstride` elements) from HBM
+// into a swizzled LDS tile; rows at or past `valid` are filled with zeros.
+template <int D>
+__device__ __forceinline__ void stage_rows(char* tile, const bf16_t* g, int64_t gstride, int rows, int valid,
+                                           int tid, int nthreads) {
+  constexpr int CH = BTile<D>::CH;
+  for (int i = tid; i < rows * CH; i += nthreads) {
+    const int r = i / CH, c = i % CH;
+    const u32x4 v = r < valid ? ld16(g + (int64_t)r * gstride + 8 * c) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(tile + BTile<D>::phys(r, c)) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dlt = rowsum(dO * O) in fp32: one row per 16 lanes (8 elements per lane at
+// D = 128; 4 or 2 lanes' worth at smaller D fold the same way).
+__global__ void __launch_bounds__(256) delta_kernel(BwdParams p, float* dlt) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b, h, i) with i fastest
+  const int sub = threadIdx.x & 15;
+  const int64_t nrows = (int64_t)p.B * p.Hq * p.S;
+  float acc = 0.f;
+  int64_t b = 0, h = 0, i = 0;
+  if (row < nrows) {
+    i = row % p.S;
+    h = (row / p.S) % p.Hq;
+    b = row / ((int64_t)p.S * p.Hq);
+    const int64_t off = b * p.q_sb + i * p.q_ss + h * p.q_sh;
+    for (int c = sub; c < p.D / 8; c += 16) {
+      const u32x4 a = ld16(reinterpret_cast<const bf16_t*>(p.dO) + off + 8 * c);
+      const u32x4 o = ld16(reinterpret_cast<const bf16_t*>(p.o) + off + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(bf16_lo(a[e]), bf16_lo(o[e]), acc);
+        acc = fmaf(bf16_hi(a[e]), bf16_hi(o[e]), acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < nrows && sub == 0) dlt[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+constexpr int kKeysPerWave = 32;
+constexpr int kDkdvWaves = 4;
+constexpr int kKeyBlock = kKeysPerWave * kDkdvWaves;  // 128 keys per workgroup
+constexpr int kQB = 32;                                // query rows per step
+
+template <int D>
+struct DkdvLds {
+  static constexpr int K = 0;                                      // [128][D]
+  static constexpr int V = K + kKeyBlock * D * 2;                  // [128][D]
+  static constexpr int Q = V + kKeyBlock * D * 2;                  // [32][D]
+  static constexpr int DO = Q + kQB * D * 2;                       // [32][D]
+  static constexpr int LSE = DO + kQB * D * 2;                     // [32] fp32, log2 units
+  static constexpr int DLT = LSE + kQB * 4;                        // [32] fp32
+  static constexpr int BYTES = DLT + kQB * 4;
+};
+
+template <int D>
+__global__ void __launch_bounds__(64 * kDkdvWaves, 1) dkdv_kernel(BwdParams p, const float* dlt) {
+  using T = BTile<D>;
+  using L = DkdvLds<D>;
+  constexpr int KS = T::KS, DB = T::DB;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int nkb = (p.S + kKeyBlock - 1) / kKeyBlock;
+  const int kblk = blockIdx.x % nkb;
+  const int kvh = (blockIdx.x / nkb) % p.Hkv;
+  const int b = blockIdx.x / (nkb * p.Hkv);
+  const int group = p.Hq / p.Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int key_blk0 = kblk * kKeyBlock;
+  const int key0 = key_blk0 + wave * kKeysPerWave;  // this wave's first key
+  const float c = p.scale * kAttnLog2e;
+
+  const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
+  const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
+  const int nvalid = min(kKeyBlock, p.S - key_blk0);
+  stage_rows<D>(lds + L::K, kg + (int64_t)key_blk0 * p.kv_ss, p.kv_ss, kKeyBlock, nvalid, tid, 64 * kDkdvWaves);
+  stage_rows<D>(lds + L::V, vg + (int64_t)key_blk0 * p.kv_ss, p.kv_ss, kKeyBlock, nvalid, tid, 64 * kDkdvWaves);
+
+  f32x16 acc_dv[DB], acc_dk[DB];
+#pragma unroll
+  for (int q = 0; q < DB; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_dv[q][r] = acc_dk[q][r] = 0.f;
+
+  const int nqb = (p.S + kQB - 1) / kQB;
+  const int qb_first = key_blk0 / kQB;  // query blocks before the workgroup's keys see none of them
+  const int my_key = key0 + col;        // the key this lane holds in S and dP
+  for (int hh = 0; hh < group; ++hh) {
+    const int h = kvh * group + hh;
+    const bf16_t* qg = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+    const bf16_t* dog = reinterpret_cast<const bf16_t*>(p.dO) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+    const float* lse_g = p.lse + ((int64_t)b * p.Hq + h) * p.S;
+    const float* dlt_g = dlt + ((int64_t)b * p.Hq + h) * p.S;
+    for (int qb = qb_first; qb < nqb; ++qb) {
+      const int q0 = qb * kQB;
+      const int qvalid = min(kQB, p.S - q0);
+      __syncthreads();  // the previous step's readers are done with Q, dO
+      stage_rows<D>(lds + L::Q, qg + (int64_t)q0 * p.q_ss, p.q_ss, kQB, qvalid, tid, 64 * kDkdvWaves);
+      stage_rows<D>(lds + L::DO, dog + (int64_t)q0 * p.q_ss, p.q_ss, kQB, qvalid, tid, 64 * kDkdvWaves);
+      if (tid < kQB) {
+        reinterpret_cast<float*>(lds + L::LSE)[tid] = tid < qvalid ? lse_g[q0 + tid] * kAttnLog2e : 0.f;
+        reinterpret_cast<float*>(lds + L::DLT)[tid] = tid < qvalid ? dlt_g[q0 + tid] : 0.f;
+      }
+      __syncthreads();
+      if (q0 + kQB - 1 < key0 || key0 >= p.S) continue;  // every query of the block precedes the wave's keys
+      // S = Q K^T and dP = dO V^T: lane holds key my_key; register r holds
+      // query q0 + 8(r/4) + 4half + r%4.
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 qa = row_frag<D>(lds + L::Q, col, 2 * ks + half);
+        const u32x4 kbf = row_frag<D>(lds + L::K, wave * kKeysPerWave + col, 2 * ks + half);
+        s = mfma(qa, kbf, s);
+        const u32x4 da = row_frag<D>(lds + L::DO, col, 2 * ks + half);
+        const u32x4 vbf = row_frag<D>(lds + L::V, wave * kKeysPerWave + col, 2 * ks + half);
+        dp = mfma(da, vbf, dp);
+      }
+      const float* lse_s = reinterpret_cast<const float*>(lds + L::LSE);
+      const float* dlt_s = reinterpret_cast<const float*>(lds + L::DLT);
+      u32x4 pp[2], pds[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv[2], dv2[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int r = 8 * kk + 2 * e + t;
+            const int qi = 8 * (r >> 2) + 4 * half + (r & 3);  // row inside the block
+            const bool live = q0 + qi < p.S && my_key <= q0 + qi && my_key < p.S;
+            const float w = live ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse_s[qi])) : 0.f;
+            pv[t] = w;
+            dv2[t] = w * (dp[r] - dlt_s[qi]);
+          }
+          pp[kk][e] = pack_bf16x2(pv[0], pv[1]);
+          pds[kk][e] = pack_bf16x2(dv2[0], dv2[1]);
+        }
+      // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane = key row), B =
+      // transposed dO / Q fragments (lane = column d).
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int q = 0; q < DB; ++q) {
+          acc_dv[q] = mfma(pp[kk], tr_frag<D>(lds + L::DO, q, kk, lane), acc_dv[q]);
+          acc_dk[q] = mfma(pds[kk], tr_frag<D>(lds + L::Q, q, kk, lane), acc_dk[q]);
+        }
+    }
+  }
+  // acc[q] register r holds key row key0 + 8(r/4) + 4half + r%4, column
+  // d = 32q + col.
+  bf16_t* dkg = reinterpret_cast<bf16_t*>(p.dk) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
+  bf16_t* dvg = reinterpret_cast<bf16_t*>(p.dv) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
+#pragma unroll
+  for (int q = 0; q < DB; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (key < p.S) {
+        dkg[(int64_t)key * p.kv_ss + 32 * q + col] = f32_to_bf16(acc_dk[q][r] * p.scale);
+        dvg[(int64_t)key * p.kv_ss + 32 * q + col] = f32_to_bf16(acc_dv[q][r]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+constexpr int kDqWaves = 8;
+constexpr int kDqRows = 32 * kDqWaves;  // 256 query rows per workgroup
+constexpr int kKT = 64;                 // keys per tile
+
+template <int D>
+struct DqLds {
+  static constexpr int K = 0;                   // [64][D]
+  static constexpr int V = K + kKT * D * 2;     // [64][D]
+  static constexpr int BYTES = V + kKT * D * 2;
+};
+
+template <int D>
+__global__ void __launch_bounds__(64 * kDqWaves, 1) dq_kernel(BwdParams p, const float* dlt) {
+  using T = BTile<D>;
+  using L = DqLds<D>;
+  constexpr int KS = T::KS, DB = T::DB;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int nqt = (p.S + kDqRows - 1) / kDqRows;
+  const int qt = nqt - 1 - (int)(blockIdx.x % nqt);  // heaviest tiles first
+  const int h = (blockIdx.x / nqt) % p.Hq;
+  const int b = blockIdx.x / (nqt * p.Hq);
+  const int kvh = h / (p.Hq / p.Hkv);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const float c = p.scale * kAttnLog2e;
+
+  const int s_base = qt * kDqRows + wave * 32;
+  const int qi = s_base + col;  // this lane's query row
+  const bool qvalid = qi < p.S;
+  const int64_t qoff = (int64_t)b * p.q_sb + (int64_t)qi * p.q_ss + (int64_t)h * p.q_sh;
+  u32x4 qf[KS], dof[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = qvalid ? ld16(reinterpret_cast<const bf16_t*>(p.q) + qoff + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
+    dof[ks] = qvalid ? ld16(reinterpret_cast<const bf16_t*>(p.dO) + qoff + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
+  }
+  const float lse2 = qvalid ? p.lse[((int64_t)b * p.Hq + h) * p.S + qi] * kAttnLog2e : 0.f;
+  const float dl = qvalid ? dlt[((int64_t)b * p.Hq + h) * p.S + qi] : 0.f;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int q = 0; q < DB; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+
+  const int last_row = min(p.S, (qt + 1) * kDqRows) - 1;  // the workgroup's last query
+  const int nkt = last_row / kKT + 1;
+  const int wave_last = s_base < p.S ? min(s_base + 31, p.S - 1) : -1;
+  const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
+  const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
+  for (int t = 0; t < nkt; ++t) {
+    const int j0 = t * kKT;
+    const int kvalid = min(kKT, p.S - j0);
+    __syncthreads();
+    stage_rows<D>(lds + L::K, kg + (int64_t)j0 * p.kv_ss, p.kv_ss, kKT, kvalid, tid, 64 * kDqWaves);
+    stage_rows<D>(lds + L::V, vg + (int64_t)j0 * p.kv_ss, p.kv_ss, kKT, kvalid, tid, 64 * kDqWaves);
+    __syncthreads();
+    if (wave_last < j0) continue;  // every key of the tile is after this wave's rows
+    // S^T = K Q^T and dP^T = V dO^T: lane holds query qi; block kb register r
+    // holds key j0 + 32kb + 8(r/4) + 4half + r%4.
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s[kb] = mfma(row_frag<D>(lds + L::K, 32 * kb + col, 2 * ks + half), qf[ks], s[kb]);
+        dp[kb] = mfma(row_frag<D>(lds + L::V, 32 * kb + col, 2 * ks + half), dof[ks], dp[kb]);
+      }
+    }
+    // dS^T = P^T (dP^T - Dlt), rounded to bf16 in the B-operand layout of
+    // dQ^T = K^T dS^T.
+    u32x4 pf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 8 * (kk & 1) + 2 * e + u;
+          const int key = j0 + 32 * (kk >> 1) + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool live = qvalid && key <= qi;
+          const float w = live ? __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][r], c, -lse2)) : 0.f;
+          v2[u] = w * (dp[kk >> 1][r] - dl);
+        }
+        pf[kk][e] = pack_bf16x2(v2[0], v2[1]);
+      }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int q = 0; q < DB; ++q) acc[q] = mfma(tr_frag<D>(lds + L::K, q, kk, lane), pf[kk], acc[q]);
+  }
+  // acc[q] register r holds d = 32q + 8(r/4) + 4half + r%4 of query qi.
+  if (qvalid) {
+    bf16_t* dqr = reinterpret_cast<bf16_t*>(p.dq) + qoff;
+#pragma unroll
+    for (int q = 0; q < DB; ++q)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * q + 8 * q4 + 4 * half;
+        u32x2 wv;
+        wv[0] = pack_bf16x2(acc[q][4 * q4] * p.scale, acc[q][4 * q4 + 1] * p.scale);
+        wv[1] = pack_bf16x2(acc[q][4 * q4 + 2] * p.scale, acc[q][4 * q4 + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(dqr + d) = wv;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const BwdParams& p, float* dlt, hipStream_t stream) {
+  const int nkb = (p.S + kKeyBlock - 1) / kKeyBlock;
+  hipLaunchKernelGGL(dkdv_kernel<D>, dim3((unsigned)(p.B * p.Hkv * nkb)), dim3(64 * kDkdvWaves),
+                     (size_t)DkdvLds<D>::BYTES, stream, p, (const float*)dlt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqt = (p.S + kDqRows - 1) / kDqRows;
+  hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(p.B * p.Hq * nqt)), dim3(64 * kDqWaves), (size_t)DqLds<D>::BYTES,
+                     stream, p, (const float*)dlt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int S, int Hq) {
+  return (((size_t)B * Hq * S * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_backward_bf16(const BwdParams& p, void* workspace, hipStream_t stream) {
+  float* dlt = reinterpret_cast<float*>(workspace);
+  const int64_t rows = (int64_t)p.B * p.Hq * p.S;
+  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, dlt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (p.D) {
+    case 32: return launch_d<32>(p, dlt, stream);
+    case 64: return launch_d<64>(p, dlt, stream);
+    default: return launch_d<128>(p, dlt, stream);
+  }
+}
+
+}  // namespace rgc

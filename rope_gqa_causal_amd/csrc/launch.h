@@ -19,6 +19,7 @@ struct RopeParams {
   int B, S, H, D;
   int64_t sb, ss, sh;
   const int32_t* pos0;
+  float sin_sign;                 // +1: rotate by the angle; -1: rotate back (the gradient)
   double theta[kMaxRopeDim / 2];  // base^(-2i/D), formed on the host in fp64
 };
 hipError_t launch_rope(const RopeParams& p, int dtype, int style, hipStream_t stream);
@@ -86,6 +87,26 @@ struct DiffParams {
   float lambda;
 };
 hipError_t launch_diff_bf16(const DiffParams& p, hipStream_t stream);
+
+// Gradients of causal GQA self-attention: q, o, dO, dq share one layout
+// [B,S,Hq,D]; k, v, dk, dv share [B,S,Hkv,D]; lse [B,Hq,S] from the forward.
+struct BwdParams {
+  void* dq;
+  void* dk;
+  void* dv;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  int B, S, Hq, Hkv, D;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t kv_sb, kv_ss, kv_sh;
+  float scale;
+};
+size_t backward_workspace_bytes(int B, int S, int Hq);
+hipError_t launch_backward_bf16(const BwdParams& p, void* workspace, hipStream_t stream);
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len);
 hipError_t launch_decode_bf16(const AttnParams& p, void* ws, hipStream_t stream);

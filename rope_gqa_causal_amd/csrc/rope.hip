@@ -137,14 +137,16 @@ struct Chunk {
 };
 
 // Sin and cos of pair i of the workgroup's tokens, tl-major, into LDS.
+// sin_sign -1 turns by minus the angle: the gradient through RoPE.
 __device__ __forceinline__ void token_table(const double* theta, const int32_t* pos0, int64_t tok0, int tpb,
-                                            int64_t ntok, int S, int half, float* sn, float* cs) {
+                                            int64_t ntok, int S, int half, float sin_sign, float* sn, float* cs) {
   for (int t = threadIdx.x; t < tpb * half; t += kBlock) {
     const int tl = t / half, i = t % half;
     const int64_t tok = tok0 + tl;
     if (tok >= ntok) break;
     const int b = (int)(tok / S), s = (int)(tok % S);
     angle_sincos((double)((pos0 ? pos0[b] : 0) + s) * theta[i], &sn[t], &cs[t]);
+    sn[t] *= sin_sign;
   }
   __syncthreads();
 }
@@ -156,7 +158,7 @@ __global__ void __launch_bounds__(kBlock) rope_vec_kernel(RopeParams p, int tpb)
   __shared__ float sn_t[kTableFloats], cs_t[kTableFloats];
   const int half = p.D / 2, cpt = p.D / (2 * E);
   const int64_t ntok = (int64_t)p.B * p.S, tok0 = (int64_t)blockIdx.x * tpb;
-  token_table(p.theta, p.pos0, tok0, tpb, ntok, p.S, half, sn_t, cs_t);
+  token_table(p.theta, p.pos0, tok0, tpb, ntok, p.S, half, p.sin_sign, sn_t, cs_t);
   const int U = p.H * cpt;
   for (int u = threadIdx.x; u < tpb * U; u += kBlock) {
     const int tl = u / U, h = (u % U) / cpt, c = u % cpt;
@@ -189,6 +191,7 @@ __global__ void __launch_bounds__(256) rope_scalar_kernel(RopeParams p) {
   const double pos = (double)((p.pos0 ? p.pos0[b] : 0) + s);
   float sn, cs;
   angle_sincos(pos * p.theta[i], &sn, &cs);
+  sn *= p.sin_sign;
   const int ia = (STYLE == ROPE_HALF) ? i : 2 * i;
   const int ib = (STYLE == ROPE_HALF) ? i + half : 2 * i + 1;
   T* base = reinterpret_cast<T*>(p.x) + (int64_t)b * p.sb + (int64_t)s * p.ss;
@@ -213,7 +216,7 @@ __global__ void __launch_bounds__(kBlock) rope_append_kernel(RopeAppendParams p,
   __shared__ float sn_t[kTableFloats], cs_t[kTableFloats];
   const int half = p.D / 2, cpt = p.D / (2 * E);
   const int64_t ntok = (int64_t)p.B * p.S, tok0 = (int64_t)blockIdx.x * tpb;
-  token_table(p.theta, p.pos0, tok0, tpb, ntok, p.S, half, sn_t, cs_t);
+  token_table(p.theta, p.pos0, tok0, tpb, ntok, p.S, half, 1.f, sn_t, cs_t);
   const int U = (p.Hq + 2 * p.Hkv) * cpt;
   for (int u = threadIdx.x; u < tpb * U; u += kBlock) {
     const int tl = u / U, h = (u % U) / cpt, c = u % cpt;

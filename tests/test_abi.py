@@ -29,7 +29,8 @@ def test_header_symbols_are_exported():
     assert {"rgc_rope_apply", "rgc_kv_cache_append", "rgc_rope_append", "rgc_norm_rope_append",
             "rgc_gqa_attn_prefill",
             "rgc_gqa_attn_decode", "rgc_gqa_attn_decode_workspace_size",
-            "rgc_diff_attn_prefill", "rgc_gqa_attn_prefill_varlen"} <= set(names)
+            "rgc_diff_attn_prefill", "rgc_gqa_attn_prefill_varlen", "rgc_rope_backward",
+            "rgc_gqa_attn_backward", "rgc_gqa_attn_backward_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -109,6 +110,29 @@ def test_varlen_rejects_bad_arguments_before_launch():
     assert _varlen(kv_ts=127) == LAYOUT
     assert _varlen(n=0) == OK
     assert _varlen(T=0, maxlen=0) == OK
+
+
+def _bwd(**kw):
+    a = dict(dq=A, dk=A, dv=A, q=A, k=A, v=A, o=A, do=A, lse=A, dt=BF16, B=2, S=16, Hq=4, Hkv=2, D=64,
+             q_sb=16 * 4 * 64, q_ss=4 * 64, q_sh=64, kv_sb=16 * 2 * 64, kv_ss=2 * 64, kv_sh=64, scale=0.125,
+             ws=A, ws_bytes=1 << 20)
+    a.update(kw)
+    return rgc.library().rgc_gqa_attn_backward(
+        a["dq"], a["dk"], a["dv"], a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dt"], a["B"], a["S"],
+        a["Hq"], a["Hkv"], a["D"], a["q_sb"], a["q_ss"], a["q_sh"], a["kv_sb"], a["kv_ss"], a["kv_sh"],
+        a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+def test_backward_rejects_bad_arguments_before_launch():
+    assert _bwd(Hq=3) == GROUP
+    assert _bwd(dt=F32) == DTYPE
+    assert _bwd(D=96) == HEADDIM
+    assert _bwd(lse=None) == NULL
+    assert _bwd(dk=A + 4) == LAYOUT
+    assert _bwd(ws_bytes=16) == WORKSPACE
+    assert _bwd(ws=A + 16) == LAYOUT
+    assert _bwd(B=0) == OK
+    assert rgc.library().rgc_gqa_attn_backward_workspace_size(2, 16, 4) >= 2 * 16 * 4 * 4
 
 
 def _decode(**kw):
