@@ -14,7 +14,9 @@
 //  * delta_kernel: Dlt_i = dO_i . o_i (fp32) per (sequence, head, row);
 //  * dkdv_kernel: a workgroup owns 128 keys of one (sequence, KV head) (32
 //    per wave, K and V in LDS) and walks every query head of the group and
-//    every query block of 32 rows at or after its keys: S = Q K^T and
+//    every query block of 64 rows at or after its keys (the next block's
+//    rows fetched into registers a step ahead, two LDS slots, one barrier a
+//    step): S = Q K^T and
 //    dP = dO V^T with keys in the MFMA N dimension, so each lane holds one
 //    key and P, dS are already the A operand of dV += P^T dO and
 //    dK += dS^T Q; dO and Q enter those as transposed fragments
@@ -114,44 +116,178 @@ __global__ void __launch_bounds__(256) delta_kernel(BwdParams p, float* dlt) {
 }
 
 // ---------------------------------------------------------------------------
+// A thread's share of a rows x D tile, fetched into registers ahead of use
+// and stored into a swizzled LDS tile after the current step's arithmetic.
+// The loads are unconditional (rows past `valid` re-read row valid - 1) so
+// that nothing waits for them before the store; the store writes zeros for
+// those rows.  Row offsets are 32-bit byte offsets from a uniform base (the
+// host keeps the row stride below 2^24 elements).
+template <int D, int ROWS, int NT>
+struct TileRegs {
+  static constexpr int N = ROWS * BTile<D>::CH / NT;  // 16-byte chunks per thread
+  static_assert(N * NT == ROWS * BTile<D>::CH, "tile chunks must split evenly over the threads");
+  u32x4 r[N];
+  __device__ __forceinline__ void fetch(const char* g, uint32_t row_bytes, int valid, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + i * NT, c = idx % BTile<D>::CH;
+      const uint32_t row = (uint32_t)min(idx / BTile<D>::CH, valid - 1);
+      r[i] = ld16(g + (row * row_bytes + 16u * (uint32_t)c));
+    }
+  }
+  __device__ __forceinline__ void store(char* tile, int valid, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + i * NT, row = idx / BTile<D>::CH, c = idx % BTile<D>::CH;
+      const u32x4 z{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(tile + BTile<D>::phys(row, c)) = row < valid ? r[i] : z;
+    }
+  }
+};
+
 constexpr int kKeysPerWave = 32;
 constexpr int kDkdvWaves = 4;
+constexpr int kDkdvThreads = 64 * kDkdvWaves;
 constexpr int kKeyBlock = kKeysPerWave * kDkdvWaves;  // 128 keys per workgroup
-constexpr int kQB = 32;                                // query rows per step
+constexpr int kQB = 64;                                // query rows per step
 
+// Two slots of (Q, dO, lse, Dlt) for the current and the next query step,
+// then K and V of the workgroup's keys (read once, into registers).  The
+// slots come first so that every per-step LDS address is a per-lane offset
+// plus an immediate below 64 KiB.
 template <int D>
 struct DkdvLds {
-  static constexpr int K = 0;                                      // [128][D]
-  static constexpr int V = K + kKeyBlock * D * 2;                  // [128][D]
-  static constexpr int Q = V + kKeyBlock * D * 2;                  // [32][D]
-  static constexpr int DO = Q + kQB * D * 2;                       // [32][D]
-  static constexpr int LSE = DO + kQB * D * 2;                     // [32] fp32, log2 units
-  static constexpr int DLT = LSE + kQB * 4;                        // [32] fp32
-  static constexpr int BYTES = DLT + kQB * 4;
+  static constexpr int Q = 0;                              // slot-relative: [64][D]
+  static constexpr int DO = Q + kQB * D * 2;               // [64][D]
+  static constexpr int LSE = DO + kQB * D * 2;             // [64] fp32, log2 units
+  static constexpr int DLT = LSE + kQB * 4;                // [64] fp32
+  static constexpr int SLOT_BYTES = DLT + kQB * 4;
+  static constexpr int K = 2 * SLOT_BYTES;                 // [128][D]
+  static constexpr int V = K + kKeyBlock * D * 2;          // [128][D]
+  static constexpr int BYTES = V + kKeyBlock * D * 2;
+};
+
+// The staged inputs of one query step: rows of Q and dO, lse and Dlt of its
+// 64 queries, and how many of them exist.
+template <int D>
+struct StepRegs {
+  TileRegs<D, kQB, kDkdvThreads> q, d_o;
+  float lse, dlt;
+  int valid;
 };
 
 template <int D>
-__global__ void __launch_bounds__(64 * kDkdvWaves, 1) dkdv_kernel(BwdParams p, const float* dlt) {
+__device__ __forceinline__ void fetch_step(StepRegs<D>& st, const BwdParams& p, const float* dlt, int b, int h,
+                                           int q0, int tid) {
+  st.valid = min(kQB, p.S - q0);
+  const int64_t off = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)q0 * p.q_ss;
+  const uint32_t row_bytes = (uint32_t)p.q_ss * 2u;
+  st.q.fetch(reinterpret_cast<const char*>(reinterpret_cast<const bf16_t*>(p.q) + off), row_bytes, st.valid, tid);
+  st.d_o.fetch(reinterpret_cast<const char*>(reinterpret_cast<const bf16_t*>(p.dO) + off), row_bytes, st.valid,
+               tid);
+  const int64_t row0 = ((int64_t)b * p.Hq + h) * p.S + q0;
+  const uint32_t i = (uint32_t)min(tid & (kQB - 1), st.valid - 1);
+  st.lse = p.lse[row0 + i];
+  st.dlt = dlt[row0 + i];
+}
+
+template <int D>
+__device__ __forceinline__ void store_step(const StepRegs<D>& st, char* slot, int tid) {
+  using L = DkdvLds<D>;
+  st.q.store(slot + L::Q, st.valid, tid);
+  st.d_o.store(slot + L::DO, st.valid, tid);
+  if (tid < kQB) {
+    const bool ok = tid < st.valid;
+    reinterpret_cast<float*>(slot + L::LSE)[tid] = ok ? st.lse * kAttnLog2e : 0.f;
+    reinterpret_cast<float*>(slot + L::DLT)[tid] = ok ? st.dlt : 0.f;
+  }
+}
+
+// One 32-query half (qm) of a step for one wave: S = Q K^T and dP = dO V^T
+// with the wave's 32 keys in the MFMA N dimension (lane holds key my_key;
+// register r holds query q0 + 32qm + 8(r/4) + 4half + r%4), the weights and
+// dS rounded to bf16 as A operands, then dV += P^T dO and dK += dS^T Q with
+// transposed dO / Q fragments as B operands.  MASK zeroes the pairs with
+// query < key and rows past S; steps where every pair is live skip it.
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_unit(const char* slot, int qm, int q0, int S, int my_key, float c, int lane,
+                                          const u32x4* kf, const u32x4* vf, f32x16* acc_dv, f32x16* acc_dk) {
+  using L = DkdvLds<D>;
+  constexpr int KS = BTile<D>::KS, DB = BTile<D>::DB;
+  const int col = lane & 31, half = lane >> 5;
+  f32x16 sm, dp;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sm[r] = dp[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    sm = mfma(row_frag<D>(slot + L::Q, 32 * qm + col, 2 * ks + half), kf[ks], sm);
+    dp = mfma(row_frag<D>(slot + L::DO, 32 * qm + col, 2 * ks + half), vf[ks], dp);
+  }
+  u32x4 pp[2], pds[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    // lse and Dlt of rows 32qm + 16kk + 4half + (0..3) and + 8 + (0..3).
+    const int qa = 32 * qm + 16 * kk + 4 * half;
+    const f32x4 la = *reinterpret_cast<const f32x4*>(slot + L::LSE + 4 * qa);
+    const f32x4 lb = *reinterpret_cast<const f32x4*>(slot + L::LSE + 4 * (qa + 8));
+    const f32x4 da = *reinterpret_cast<const f32x4*>(slot + L::DLT + 4 * qa);
+    const f32x4 db = *reinterpret_cast<const f32x4*>(slot + L::DLT + 4 * (qa + 8));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float pv[2], dv2[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = 8 * kk + 2 * e + t;  // rows qa + (r & 3) or qa + 8 + (r & 3)
+        const float l = (r & 4) ? lb[r & 3] : la[r & 3];
+        const float d = (r & 4) ? db[r & 3] : da[r & 3];
+        const float w = __builtin_amdgcn_exp2f(fmaf(sm[r], c, -l));
+        if (MASK) {
+          const int qrow = q0 + 32 * qm + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool live = qrow < S && my_key <= qrow;
+          pv[t] = live ? w : 0.f;
+          dv2[t] = live ? w * (dp[r] - d) : 0.f;
+        } else {
+          pv[t] = w;
+          dv2[t] = w * (dp[r] - d);
+        }
+      }
+      pp[kk][e] = pack_bf16x2(pv[0], pv[1]);
+      pds[kk][e] = pack_bf16x2(dv2[0], dv2[1]);
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int q = 0; q < DB; ++q) {
+      acc_dv[q] = mfma(pp[kk], tr_frag<D>(slot + L::DO, q, 2 * qm + kk, lane), acc_dv[q]);
+      acc_dk[q] = mfma(pds[kk], tr_frag<D>(slot + L::Q, q, 2 * qm + kk, lane), acc_dk[q]);
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kDkdvThreads, 1) dkdv_kernel(BwdParams p, const float* dlt) {
   using T = BTile<D>;
   using L = DkdvLds<D>;
   constexpr int KS = T::KS, DB = T::DB;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int nkb = (p.S + kKeyBlock - 1) / kKeyBlock;
-  const int kblk = blockIdx.x % nkb;
-  const int kvh = (blockIdx.x / nkb) % p.Hkv;
-  const int b = blockIdx.x / (nkb * p.Hkv);
+  // Key blocks in order of work, the first (which meets every query block)
+  // first, so that the last workgroups to start are the short ones.
+  const int kblk = blockIdx.x / (p.B * p.Hkv);
+  const int kvh = blockIdx.x % p.Hkv;
+  const int b = (blockIdx.x / p.Hkv) % p.B;
   const int group = p.Hq / p.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int key_blk0 = kblk * kKeyBlock;
   const int key0 = key_blk0 + wave * kKeysPerWave;  // this wave's first key
+  const int my_key = key0 + col;                      // the key this lane holds in S and dP
   const float c = p.scale * kAttnLog2e;
 
   const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
   const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
   const int nvalid = min(kKeyBlock, p.S - key_blk0);
-  stage_rows<D>(lds + L::K, kg + (int64_t)key_blk0 * p.kv_ss, p.kv_ss, kKeyBlock, nvalid, tid, 64 * kDkdvWaves);
-  stage_rows<D>(lds + L::V, vg + (int64_t)key_blk0 * p.kv_ss, p.kv_ss, kKeyBlock, nvalid, tid, 64 * kDkdvWaves);
+  stage_rows<D>(lds + L::K, kg + (int64_t)key_blk0 * p.kv_ss, p.kv_ss, kKeyBlock, nvalid, tid, kDkdvThreads);
+  stage_rows<D>(lds + L::V, vg + (int64_t)key_blk0 * p.kv_ss, p.kv_ss, kKeyBlock, nvalid, tid, kDkdvThreads);
 
   f32x16 acc_dv[DB], acc_dk[DB];
 #pragma unroll
@@ -159,71 +295,49 @@ __global__ void __launch_bounds__(64 * kDkdvWaves, 1) dkdv_kernel(BwdParams p, c
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_dv[q][r] = acc_dk[q][r] = 0.f;
 
+  // Steps n = (query head hh, query block qb of 64 rows) over the blocks at
+  // or after the workgroup's first key; each step's rows are fetched into
+  // registers one step ahead and stored into the other LDS slot after the
+  // arithmetic.  Steps alternate between the two slots, two per iteration,
+  // so that slot addresses are compile-time offsets.
   const int nqb = (p.S + kQB - 1) / kQB;
-  const int qb_first = key_blk0 / kQB;  // query blocks before the workgroup's keys see none of them
-  const int my_key = key0 + col;        // the key this lane holds in S and dP
-  for (int hh = 0; hh < group; ++hh) {
-    const int h = kvh * group + hh;
-    const bf16_t* qg = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
-    const bf16_t* dog = reinterpret_cast<const bf16_t*>(p.dO) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
-    const float* lse_g = p.lse + ((int64_t)b * p.Hq + h) * p.S;
-    const float* dlt_g = dlt + ((int64_t)b * p.Hq + h) * p.S;
-    for (int qb = qb_first; qb < nqb; ++qb) {
-      const int q0 = qb * kQB;
-      const int qvalid = min(kQB, p.S - q0);
-      __syncthreads();  // the previous step's readers are done with Q, dO
-      stage_rows<D>(lds + L::Q, qg + (int64_t)q0 * p.q_ss, p.q_ss, kQB, qvalid, tid, 64 * kDkdvWaves);
-      stage_rows<D>(lds + L::DO, dog + (int64_t)q0 * p.q_ss, p.q_ss, kQB, qvalid, tid, 64 * kDkdvWaves);
-      if (tid < kQB) {
-        reinterpret_cast<float*>(lds + L::LSE)[tid] = tid < qvalid ? lse_g[q0 + tid] * kAttnLog2e : 0.f;
-        reinterpret_cast<float*>(lds + L::DLT)[tid] = tid < qvalid ? dlt_g[q0 + tid] : 0.f;
-      }
-      __syncthreads();
-      if (q0 + kQB - 1 < key0 || key0 >= p.S) continue;  // every query of the block precedes the wave's keys
-      // S = Q K^T and dP = dO V^T: lane holds key my_key; register r holds
-      // query q0 + 8(r/4) + 4half + r%4.
-      f32x16 s, dp;
+  const int qb_first = key_blk0 / kQB;
+  const int nsteps = group * (nqb - qb_first);
+  int hh = 0, qb = qb_first;  // the step being computed
+  StepRegs<D> st;
+  fetch_step<D>(st, p, dlt, b, kvh * group, qb * kQB, tid);
+  store_step<D>(st, lds, tid);
+  __syncthreads();
+  // This wave's K and V rows stay in registers as the B operands of S and dP.
+  u32x4 kf[KS], vf[KS];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 qa = row_frag<D>(lds + L::Q, col, 2 * ks + half);
-        const u32x4 kbf = row_frag<D>(lds + L::K, wave * kKeysPerWave + col, 2 * ks + half);
-        s = mfma(qa, kbf, s);
-        const u32x4 da = row_frag<D>(lds + L::DO, col, 2 * ks + half);
-        const u32x4 vbf = row_frag<D>(lds + L::V, wave * kKeysPerWave + col, 2 * ks + half);
-        dp = mfma(da, vbf, dp);
-      }
-      const float* lse_s = reinterpret_cast<const float*>(lds + L::LSE);
-      const float* dlt_s = reinterpret_cast<const float*>(lds + L::DLT);
-      u32x4 pp[2], pds[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv[2], dv2[2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int r = 8 * kk + 2 * e + t;
-            const int qi = 8 * (r >> 2) + 4 * half + (r & 3);  // row inside the block
-            const bool live = q0 + qi < p.S && my_key <= q0 + qi && my_key < p.S;
-            const float w = live ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse_s[qi])) : 0.f;
-            pv[t] = w;
-            dv2[t] = w * (dp[r] - dlt_s[qi]);
-          }
-          pp[kk][e] = pack_bf16x2(pv[0], pv[1]);
-          pds[kk][e] = pack_bf16x2(dv2[0], dv2[1]);
-        }
-      // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane = key row), B =
-      // transposed dO / Q fragments (lane = column d).
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int q = 0; q < DB; ++q) {
-          acc_dv[q] = mfma(pp[kk], tr_frag<D>(lds + L::DO, q, kk, lane), acc_dv[q]);
-          acc_dk[q] = mfma(pds[kk], tr_frag<D>(lds + L::Q, q, kk, lane), acc_dk[q]);
-        }
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = row_frag<D>(lds + L::K, wave * kKeysPerWave + col, 2 * ks + half);
+    vf[ks] = row_frag<D>(lds + L::V, wave * kKeysPerWave + col, 2 * ks + half);
+  }
+  auto step = [&](auto slot_tag, int n) {
+    constexpr int SL = decltype(slot_tag)::value;
+    const int q0 = qb * kQB;
+    int nhh = hh, nqb_ = qb + 1;
+    if (nqb_ == nqb) nqb_ = qb_first, ++nhh;
+    const bool more = n + 1 < nsteps;
+    if (more) fetch_step<D>(st, p, dlt, b, kvh * group + nhh, nqb_ * kQB, tid);
+    const char* slot = lds + SL * L::SLOT_BYTES;
+    if (q0 >= key0 + kKeysPerWave - 1 && q0 + kQB <= p.S) {  // every pair of the step is live
+      dkdv_unit<D, false>(slot, 0, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
+      dkdv_unit<D, false>(slot, 1, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
+    } else {
+      dkdv_unit<D, true>(slot, 0, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
+      dkdv_unit<D, true>(slot, 1, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
     }
+    if (more) store_step<D>(st, lds + (SL ^ 1) * L::SLOT_BYTES, tid);
+    __syncthreads();
+    hh = nhh;
+    qb = nqb_;
+  };
+  for (int n = 0; n < nsteps; n += 2) {
+    step(std::integral_constant<int, 0>{}, n);
+    if (n + 1 < nsteps) step(std::integral_constant<int, 1>{}, n + 1);
   }
   // acc[q] register r holds key row key0 + 8(r/4) + 4half + r%4, column
   // d = 32q + col.
@@ -355,7 +469,7 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) dq_kernel(BwdParams p, const
 template <int D>
 hipError_t launch_d(const BwdParams& p, float* dlt, hipStream_t stream) {
   const int nkb = (p.S + kKeyBlock - 1) / kKeyBlock;
-  hipLaunchKernelGGL(dkdv_kernel<D>, dim3((unsigned)(p.B * p.Hkv * nkb)), dim3(64 * kDkdvWaves),
+  hipLaunchKernelGGL(dkdv_kernel<D>, dim3((unsigned)(p.B * p.Hkv * nkb)), dim3(kDkdvThreads),
                      (size_t)DkdvLds<D>::BYTES, stream, p, (const float*)dlt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

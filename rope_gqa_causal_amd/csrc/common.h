@@ -30,10 +30,9 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
 // Two fp32 -> two bf16 packed in one dword (first in the low half), rounded
 // to nearest even by the hardware conversion (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  bf16x2 v;
-  v[0] = (__bf16)lo;
-  v[1] = (__bf16)hi;
-  return __builtin_bit_cast(uint32_t, v);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(bf16_t, (__bf16)x);
