@@ -240,8 +240,8 @@ int rgc_gqa_attn_prefill_varlen(void* o, const void* q, const void* k, const voi
  *                    (rgc_gqa_attn_prefill's lse output, natural log).
  *   workspace        >= rgc_gqa_attn_backward_workspace_size bytes,
  *                    256-byte aligned, caller-owned scratch.
- * bf16 only (RGC_ERR_DTYPE); head dim 32, 64 or 128.  The token stride
- * q_ss must lie in [0, 2^24) elements (RGC_ERR_LAYOUT otherwise).  The
+ * bf16 only (RGC_ERR_DTYPE); head dim 32, 64 or 128.  The token strides
+ * q_ss and kv_ss must lie in [0, 2^24) elements (RGC_ERR_LAYOUT otherwise).  The
  * weights are recomputed from lse; P and dS are rounded to bf16 for the matrix cores and
  * accumulate in fp32.  For the gradient with respect to the unrotated q and
  * k, apply rgc_rope_backward to dq and dk.

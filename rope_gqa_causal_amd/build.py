@@ -23,13 +23,22 @@ FLAGS = [
 ]
 
 
+# Per-file scheduler choice: the backward kernels run one wave per SIMD and
+# need their LDS reads issued several matrix instructions ahead, which the
+# ILP-oriented machine scheduler does and the default (occupancy-oriented)
+# one does not.
+FILE_FLAGS = {
+    "backward.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src, verbose):
     obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -325,7 +325,8 @@ int rgc_gqa_attn_backward(void* dq, void* dk, void* dv, const void* q, const voi
       !stride_ok(kv_sb, dtype) || !stride_ok(kv_ss, dtype) || !stride_ok(kv_sh, dtype))
     return RGC_ERR_LAYOUT;
   if ((int64_t)B * S * Hq > 0x7FFFFFFFLL) return RGC_ERR_SHAPE;
-  if (q_ss < 0 || q_ss >= (int64_t(1) << 24)) return RGC_ERR_LAYOUT;  // 32-bit row offsets in the kernels
+  if (q_ss < 0 || q_ss >= (int64_t(1) << 24) || kv_ss < 0 || kv_ss >= (int64_t(1) << 24))
+    return RGC_ERR_LAYOUT;  // 32-bit row offsets in the kernels
   const size_t need = backward_workspace_bytes(B, S, Hq);
   if (!workspace || ws_bytes < need) return RGC_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RGC_ERR_LAYOUT;

@@ -36,17 +36,27 @@
 namespace rgc {
 namespace {
 
-// Row-major bf16 tiles in LDS: 16-byte chunk c of row r sits at chunk
-// c ^ (r % CH), so 16-byte row fragments of 32 consecutive rows are
-// conflict-free.  Transposed fragments read the same layout through
-// per-lane addresses.
+// Row-major bf16 tiles in LDS with 16-byte chunk c of row r stored at chunk
+// c ^ swz(r).  With 64 four-byte banks (256 bytes), a 16-byte row fragment
+// read covers 16 consecutive rows at one chunk, and a transposed fragment
+// read (8 bytes a lane, 32 lanes at a time) covers 4 consecutive rows at 4
+// consecutive chunks of an aligned group of 4.  swz is a bijection of the
+// row's position among the rows that share a 256-byte bank line (so the
+// first read meets every bank once), and it sends the 4 rows of the second
+// read to different 4-chunk groups when they share a line (D = 128: one row
+// per line; D = 64: two).
 template <int D>
 struct BTile {
   static constexpr int CH = D / 8;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int ROW_BYTES = D * 2;
-  static __device__ __forceinline__ int phys(int r, int c) { return r * ROW_BYTES + 16 * (c ^ (r % CH)); }
+  static __device__ __forceinline__ int swz(int r) {
+    if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    if (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    return (r >> 2) & 3;
+  }
+  static __device__ __forceinline__ int phys(int r, int c) { return r * ROW_BYTES + 16 * (c ^ swz(r)); }
 };
 
 // 16-byte row fragment: row r, logical chunk c.
@@ -124,13 +134,14 @@ __global__ void __launch_bounds__(256) delta_kernel(BwdParams p, float* dlt) {
 // host keeps the row stride below 2^24 elements).
 template <int D, int ROWS, int NT>
 struct TileRegs {
-  static constexpr int N = ROWS * BTile<D>::CH / NT;  // 16-byte chunks per thread
-  static_assert(N * NT == ROWS * BTile<D>::CH, "tile chunks must split evenly over the threads");
+  static constexpr int CHUNKS = ROWS * BTile<D>::CH;
+  static constexpr int N = (CHUNKS + NT - 1) / NT;  // 16-byte chunks per thread
+  static_assert(CHUNKS % NT == 0 || CHUNKS < NT, "tile chunks must split evenly over the threads");
   u32x4 r[N];
   __device__ __forceinline__ void fetch(const char* g, uint32_t row_bytes, int valid, int tid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int idx = tid + i * NT, c = idx % BTile<D>::CH;
+      const int idx = min(tid + i * NT, CHUNKS - 1), c = idx % BTile<D>::CH;
       const uint32_t row = (uint32_t)min(idx / BTile<D>::CH, valid - 1);
       r[i] = ld16(g + (row * row_bytes + 16u * (uint32_t)c));
     }
@@ -140,7 +151,8 @@ struct TileRegs {
     for (int i = 0; i < N; ++i) {
       const int idx = tid + i * NT, row = idx / BTile<D>::CH, c = idx % BTile<D>::CH;
       const u32x4 z{0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(tile + BTile<D>::phys(row, c)) = row < valid ? r[i] : z;
+      if (CHUNKS % NT == 0 || idx < CHUNKS)
+        *reinterpret_cast<u32x4*>(tile + BTile<D>::phys(row, c)) = row < valid ? r[i] : z;
     }
   }
 };
@@ -203,27 +215,34 @@ __device__ __forceinline__ void store_step(const StepRegs<D>& st, char* slot, in
   }
 }
 
-// One 32-query half (qm) of a step for one wave: S = Q K^T and dP = dO V^T
-// with the wave's 32 keys in the MFMA N dimension (lane holds key my_key;
-// register r holds query q0 + 32qm + 8(r/4) + 4half + r%4), the weights and
-// dS rounded to bf16 as A operands, then dV += P^T dO and dK += dS^T Q with
-// transposed dO / Q fragments as B operands.  MASK zeroes the pairs with
-// query < key and rows past S; steps where every pair is live skip it.
-template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_unit(const char* slot, int qm, int q0, int S, int my_key, float c, int lane,
-                                          const u32x4* kf, const u32x4* vf, f32x16* acc_dv, f32x16* acc_dk) {
+// The arithmetic of one step for one wave, in two 32-query halves qm:
+// S = Q K^T and dP = dO V^T with the wave's 32 keys in the MFMA N dimension
+// (lane holds key my_key; register r holds query q0 + 32qm + 8(r/4) + 4half
+// + r%4), the weights P and dS = P (dP - Dlt) rounded to bf16 as A operands,
+// then dV += P^T dO and dK += dS^T Q with transposed dO / Q fragments as B
+// operands.  Both halves' scores are issued first, so that the matrix cores
+// can work on the second half while the vector unit forms the first half's
+// weights.  MASK zeroes the pairs with query < key and rows past S; steps
+// where every pair is live skip it.
+template <int D>
+__device__ __forceinline__ void dkdv_scores(const char* slot, int qm, int lane, const u32x4* kf, const u32x4* vf,
+                                            f32x16& sm, f32x16& dp) {
   using L = DkdvLds<D>;
-  constexpr int KS = BTile<D>::KS, DB = BTile<D>::DB;
   const int col = lane & 31, half = lane >> 5;
-  f32x16 sm, dp;
 #pragma unroll
   for (int r = 0; r < 16; ++r) sm[r] = dp[r] = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int ks = 0; ks < BTile<D>::KS; ++ks) {
     sm = mfma(row_frag<D>(slot + L::Q, 32 * qm + col, 2 * ks + half), kf[ks], sm);
     dp = mfma(row_frag<D>(slot + L::DO, 32 * qm + col, 2 * ks + half), vf[ks], dp);
   }
-  u32x4 pp[2], pds[2];
+}
+
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_weights(const char* slot, int qm, int q0, int S, int my_key, float c, int lane,
+                                             const f32x16& sm, const f32x16& dp, u32x4* pp, u32x4* pds) {
+  using L = DkdvLds<D>;
+  const int half = lane >> 5;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     // lse and Dlt of rows 32qm + 16kk + 4half + (0..3) and + 8 + (0..3).
@@ -255,13 +274,32 @@ __device__ __forceinline__ void dkdv_unit(const char* slot, int qm, int q0, int 
       pds[kk][e] = pack_bf16x2(dv2[0], dv2[1]);
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_accumulate(const char* slot, int qm, int lane, const u32x4* pp, const u32x4* pds,
+                                                f32x16* acc_dv, f32x16* acc_dk) {
+  using L = DkdvLds<D>;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int q = 0; q < DB; ++q) {
+    for (int q = 0; q < BTile<D>::DB; ++q) {
       acc_dv[q] = mfma(pp[kk], tr_frag<D>(slot + L::DO, q, 2 * qm + kk, lane), acc_dv[q]);
       acc_dk[q] = mfma(pds[kk], tr_frag<D>(slot + L::Q, q, 2 * qm + kk, lane), acc_dk[q]);
     }
+}
+
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_step(const char* slot, int q0, int S, int my_key, float c, int lane,
+                                          const u32x4* kf, const u32x4* vf, f32x16* acc_dv, f32x16* acc_dk) {
+  f32x16 sm[2], dp[2];
+  u32x4 pp[2][2], pds[2][2];
+  dkdv_scores<D>(slot, 0, lane, kf, vf, sm[0], dp[0]);
+  dkdv_scores<D>(slot, 1, lane, kf, vf, sm[1], dp[1]);
+  dkdv_weights<D, MASK>(slot, 0, q0, S, my_key, c, lane, sm[0], dp[0], pp[0], pds[0]);
+  dkdv_accumulate<D>(slot, 0, lane, pp[0], pds[0], acc_dv, acc_dk);
+  dkdv_weights<D, MASK>(slot, 1, q0, S, my_key, c, lane, sm[1], dp[1], pp[1], pds[1]);
+  dkdv_accumulate<D>(slot, 1, lane, pp[1], pds[1], acc_dv, acc_dk);
 }
 
 template <int D>
@@ -323,13 +361,10 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) dkdv_kernel(BwdParams p, cons
     const bool more = n + 1 < nsteps;
     if (more) fetch_step<D>(st, p, dlt, b, kvh * group + nhh, nqb_ * kQB, tid);
     const char* slot = lds + SL * L::SLOT_BYTES;
-    if (q0 >= key0 + kKeysPerWave - 1 && q0 + kQB <= p.S) {  // every pair of the step is live
-      dkdv_unit<D, false>(slot, 0, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
-      dkdv_unit<D, false>(slot, 1, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
-    } else {
-      dkdv_unit<D, true>(slot, 0, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
-      dkdv_unit<D, true>(slot, 1, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
-    }
+    if (q0 >= key0 + kKeysPerWave - 1 && q0 + kQB <= p.S)  // every pair of the step is live
+      dkdv_step<D, false>(slot, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
+    else
+      dkdv_step<D, true>(slot, q0, p.S, my_key, c, lane, kf, vf, acc_dv, acc_dk);
     if (more) store_step<D>(st, lds + (SL ^ 1) * L::SLOT_BYTES, tid);
     __syncthreads();
     hh = nhh;
@@ -356,27 +391,83 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) dkdv_kernel(BwdParams p, cons
 }
 
 // ---------------------------------------------------------------------------
-constexpr int kDqWaves = 8;
-constexpr int kDqRows = 32 * kDqWaves;  // 256 query rows per workgroup
+constexpr int kDqWaves = 4;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqRows = 32 * kDqWaves;  // 128 query rows per workgroup
 constexpr int kKT = 64;                 // keys per tile
 
+// Two slots of (K, V) key tiles: the current one and the next, which is
+// fetched into registers during the current tile's arithmetic.
 template <int D>
 struct DqLds {
-  static constexpr int K = 0;                   // [64][D]
+  static constexpr int K = 0;                   // slot-relative: [64][D]
   static constexpr int V = K + kKT * D * 2;     // [64][D]
-  static constexpr int BYTES = V + kKT * D * 2;
+  static constexpr int SLOT_BYTES = V + kKT * D * 2;
+  static constexpr int BYTES = 2 * SLOT_BYTES;
 };
 
 template <int D>
-__global__ void __launch_bounds__(64 * kDqWaves, 1) dq_kernel(BwdParams p, const float* dlt) {
+struct KvRegs {
+  TileRegs<D, kKT, kDqThreads> k, v;
+  int valid;
+};
+
+// One 32-key half (kb) of a key tile for one wave: S^T = K Q^T and
+// dP^T = V dO^T with the wave's 32 queries in the MFMA N dimension (lane
+// holds query qi; register r holds key j0 + 32kb + 8(r/4) + 4half + r%4),
+// dS^T = P^T (dP^T - Dlt) rounded to bf16 in the B-operand layout of
+// dQ^T += K^T dS^T, with K^T read transposed from the K tile.  MASK zeroes
+// the pairs with key > query and rows past S; tiles where every pair is
+// live skip it.
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_unit(const char* slot, int kb, int j0, int qi, bool qvalid, float lse2, float dl,
+                                        float c, int lane, const u32x4* qf, const u32x4* dof, f32x16* acc) {
+  using L = DqLds<D>;
+  constexpr int KS = BTile<D>::KS, DB = BTile<D>::DB;
+  const int col = lane & 31, half = lane >> 5;
+  f32x16 sm, dp;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sm[r] = dp[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    sm = mfma(row_frag<D>(slot + L::K, 32 * kb + col, 2 * ks + half), qf[ks], sm);
+    dp = mfma(row_frag<D>(slot + L::V, 32 * kb + col, 2 * ks + half), dof[ks], dp);
+  }
+  u32x4 pf[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = 8 * kk + 2 * e + u;
+        const float w = __builtin_amdgcn_exp2f(fmaf(sm[r], c, -lse2));
+        if (MASK) {
+          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          v2[u] = qvalid && key <= qi ? w * (dp[r] - dl) : 0.f;
+        } else {
+          v2[u] = w * (dp[r] - dl);
+        }
+      }
+      pf[kk][e] = pack_bf16x2(v2[0], v2[1]);
+    }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int q = 0; q < DB; ++q) acc[q] = mfma(tr_frag<D>(slot + L::K, q, 2 * kb + kk, lane), pf[kk], acc[q]);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kDqThreads, 1) dq_kernel(BwdParams p, const float* dlt) {
   using T = BTile<D>;
   using L = DqLds<D>;
   constexpr int KS = T::KS, DB = T::DB;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int nqt = (p.S + kDqRows - 1) / kDqRows;
-  const int qt = nqt - 1 - (int)(blockIdx.x % nqt);  // heaviest tiles first
-  const int h = (blockIdx.x / nqt) % p.Hq;
-  const int b = blockIdx.x / (nqt * p.Hq);
+  const int qt = nqt - 1 - (int)(blockIdx.x / (p.B * p.Hq));  // heaviest tiles first
+  const int h = blockIdx.x % p.Hq;
+  const int b = (blockIdx.x / p.Hq) % p.B;
   const int kvh = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
@@ -404,51 +495,49 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) dq_kernel(BwdParams p, const
   const int last_row = min(p.S, (qt + 1) * kDqRows) - 1;  // the workgroup's last query
   const int nkt = last_row / kKT + 1;
   const int wave_last = s_base < p.S ? min(s_base + 31, p.S - 1) : -1;
-  const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
-  const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
-  for (int t = 0; t < nkt; ++t) {
+  const bool rows_full = s_base + 31 < p.S;
+  const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.kv_sb +
+                                                 (int64_t)kvh * p.kv_sh);
+  const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.kv_sb +
+                                                 (int64_t)kvh * p.kv_sh);
+  const uint32_t row_bytes = (uint32_t)p.kv_ss * 2u;
+  KvRegs<D> st;
+  auto fetch = [&](int j0) {
+    st.valid = min(kKT, p.S - j0);
+    const int64_t off = (int64_t)j0 * p.kv_ss * 2;
+    st.k.fetch(kg + off, row_bytes, st.valid, tid);
+    st.v.fetch(vg + off, row_bytes, st.valid, tid);
+  };
+  auto store = [&](char* slot) {
+    st.k.store(slot + L::K, st.valid, tid);
+    st.v.store(slot + L::V, st.valid, tid);
+  };
+  fetch(0);
+  store(lds);
+  __syncthreads();
+  // Key tiles alternate between the two slots, two per iteration, so that
+  // slot addresses are compile-time offsets.
+  auto step = [&](auto slot_tag, int t) {
+    constexpr int SL = decltype(slot_tag)::value;
     const int j0 = t * kKT;
-    const int kvalid = min(kKT, p.S - j0);
-    __syncthreads();
-    stage_rows<D>(lds + L::K, kg + (int64_t)j0 * p.kv_ss, p.kv_ss, kKT, kvalid, tid, 64 * kDqWaves);
-    stage_rows<D>(lds + L::V, vg + (int64_t)j0 * p.kv_ss, p.kv_ss, kKT, kvalid, tid, 64 * kDqWaves);
-    __syncthreads();
-    if (wave_last < j0) continue;  // every key of the tile is after this wave's rows
-    // S^T = K Q^T and dP^T = V dO^T: lane holds query qi; block kb register r
-    // holds key j0 + 32kb + 8(r/4) + 4half + r%4.
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s[kb] = mfma(row_frag<D>(lds + L::K, 32 * kb + col, 2 * ks + half), qf[ks], s[kb]);
-        dp[kb] = mfma(row_frag<D>(lds + L::V, 32 * kb + col, 2 * ks + half), dof[ks], dp[kb]);
+    const bool more = t + 1 < nkt;
+    if (more) fetch(j0 + kKT);
+    const char* slot = lds + SL * L::SLOT_BYTES;
+    if (wave_last >= j0) {
+      if (j0 + kKT - 1 <= s_base && rows_full) {  // every pair of the tile is live
+        dq_unit<D, false>(slot, 0, j0, qi, qvalid, lse2, dl, c, lane, qf, dof, acc);
+        dq_unit<D, false>(slot, 1, j0, qi, qvalid, lse2, dl, c, lane, qf, dof, acc);
+      } else {
+        dq_unit<D, true>(slot, 0, j0, qi, qvalid, lse2, dl, c, lane, qf, dof, acc);
+        dq_unit<D, true>(slot, 1, j0, qi, qvalid, lse2, dl, c, lane, qf, dof, acc);
       }
     }
-    // dS^T = P^T (dP^T - Dlt), rounded to bf16 in the B-operand layout of
-    // dQ^T = K^T dS^T.
-    u32x4 pf[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 8 * (kk & 1) + 2 * e + u;
-          const int key = j0 + 32 * (kk >> 1) + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool live = qvalid && key <= qi;
-          const float w = live ? __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][r], c, -lse2)) : 0.f;
-          v2[u] = w * (dp[kk >> 1][r] - dl);
-        }
-        pf[kk][e] = pack_bf16x2(v2[0], v2[1]);
-      }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int q = 0; q < DB; ++q) acc[q] = mfma(tr_frag<D>(lds + L::K, q, kk, lane), pf[kk], acc[q]);
+    if (more) store(lds + (SL ^ 1) * L::SLOT_BYTES);
+    __syncthreads();
+  };
+  for (int t = 0; t < nkt; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nkt) step(std::integral_constant<int, 1>{}, t + 1);
   }
   // acc[q] register r holds d = 32q + 8(r/4) + 4half + r%4 of query qi.
   if (qvalid) {
@@ -474,7 +563,7 @@ hipError_t launch_d(const BwdParams& p, float* dlt, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqt = (p.S + kDqRows - 1) / kDqRows;
-  hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(p.B * p.Hq * nqt)), dim3(64 * kDqWaves), (size_t)DqLds<D>::BYTES,
+  hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(p.B * p.Hq * nqt)), dim3(kDqThreads), (size_t)DqLds<D>::BYTES,
                      stream, p, (const float*)dlt);
   return hipGetLastError();
 }

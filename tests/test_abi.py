@@ -133,6 +133,7 @@ def test_backward_rejects_bad_arguments_before_launch():
     assert _bwd(ws=A + 16) == LAYOUT
     assert _bwd(q_ss=1 << 24) == LAYOUT  # row offsets are 32-bit inside the kernels
     assert _bwd(q_ss=-4 * 64) == LAYOUT
+    assert _bwd(kv_ss=1 << 24) == LAYOUT
     assert _bwd(B=0) == OK
     assert rgc.library().rgc_gqa_attn_backward_workspace_size(2, 16, 4) >= 2 * 16 * 4 * 4
 
