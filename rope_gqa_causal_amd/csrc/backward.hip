@@ -220,86 +220,120 @@ __device__ __forceinline__ void store_step(const StepRegs<D>& st, char* slot, in
 // (lane holds key my_key; register r holds query q0 + 32qm + 8(r/4) + 4half
 // + r%4), the weights P and dS = P (dP - Dlt) rounded to bf16 as A operands,
 // then dV += P^T dO and dK += dS^T Q with transposed dO / Q fragments as B
-// operands.  Both halves' scores are issued first, so that the matrix cores
-// can work on the second half while the vector unit forms the first half's
-// weights.  MASK zeroes the pairs with query < key and rows past S; steps
-// where every pair is live skip it.
-template <int D>
-__device__ __forceinline__ void dkdv_scores(const char* slot, int qm, int lane, const u32x4* kf, const u32x4* vf,
-                                            f32x16& sm, f32x16& dp) {
-  using L = DkdvLds<D>;
-  const int col = lane & 31, half = lane >> 5;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sm[r] = dp[r] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < BTile<D>::KS; ++ks) {
-    sm = mfma(row_frag<D>(slot + L::Q, 32 * qm + col, 2 * ks + half), kf[ks], sm);
-    dp = mfma(row_frag<D>(slot + L::DO, 32 * qm + col, 2 * ks + half), vf[ks], dp);
-  }
-}
+// operands.
+//
+// One wave runs per SIMD, so the step is software-pipelined by hand as a
+// fixed sequence of 4 x (2 KS) matrix-instruction slots: the first half's
+// scores, the second half's scores, the first half's dV/dK, the second
+// half's dV/dK.  Each slot's LDS operand is read kLookahead slots ahead, and
+// the weights of one score value are formed in each slot from two slots
+// after the half's scores end, so that the vector work runs under the
+// matrix instructions.  Scheduling barriers keep the compiler to this order.
+// MASK zeroes the pairs with query < key and rows past S; steps where every
+// pair is live skip it.
+constexpr int kLookahead = 3;
 
-template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_weights(const char* slot, int qm, int q0, int S, int my_key, float c, int lane,
-                                             const f32x16& sm, const f32x16& dp, u32x4* pp, u32x4* pds) {
-  using L = DkdvLds<D>;
-  const int half = lane >> 5;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    // lse and Dlt of rows 32qm + 16kk + 4half + (0..3) and + 8 + (0..3).
-    const int qa = 32 * qm + 16 * kk + 4 * half;
-    const f32x4 la = *reinterpret_cast<const f32x4*>(slot + L::LSE + 4 * qa);
-    const f32x4 lb = *reinterpret_cast<const f32x4*>(slot + L::LSE + 4 * (qa + 8));
-    const f32x4 da = *reinterpret_cast<const f32x4*>(slot + L::DLT + 4 * qa);
-    const f32x4 db = *reinterpret_cast<const f32x4*>(slot + L::DLT + 4 * (qa + 8));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float pv[2], dv2[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = 8 * kk + 2 * e + t;  // rows qa + (r & 3) or qa + 8 + (r & 3)
-        const float l = (r & 4) ? lb[r & 3] : la[r & 3];
-        const float d = (r & 4) ? db[r & 3] : da[r & 3];
-        const float w = __builtin_amdgcn_exp2f(fmaf(sm[r], c, -l));
-        if (MASK) {
-          const int qrow = q0 + 32 * qm + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool live = qrow < S && my_key <= qrow;
-          pv[t] = live ? w : 0.f;
-          dv2[t] = live ? w * (dp[r] - d) : 0.f;
-        } else {
-          pv[t] = w;
-          dv2[t] = w * (dp[r] - d);
-        }
-      }
-      pp[kk][e] = pack_bf16x2(pv[0], pv[1]);
-      pds[kk][e] = pack_bf16x2(dv2[0], dv2[1]);
-    }
+// Compile-time loop: f(std::integral_constant<int, J>) for J = B .. E - 1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
-}
-
-template <int D>
-__device__ __forceinline__ void dkdv_accumulate(const char* slot, int qm, int lane, const u32x4* pp, const u32x4* pds,
-                                                f32x16* acc_dv, f32x16* acc_dk) {
-  using L = DkdvLds<D>;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int q = 0; q < BTile<D>::DB; ++q) {
-      acc_dv[q] = mfma(pp[kk], tr_frag<D>(slot + L::DO, q, 2 * qm + kk, lane), acc_dv[q]);
-      acc_dk[q] = mfma(pds[kk], tr_frag<D>(slot + L::Q, q, 2 * qm + kk, lane), acc_dk[q]);
-    }
 }
 
 template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_step(const char* slot, int q0, int S, int my_key, float c, int lane,
                                           const u32x4* kf, const u32x4* vf, f32x16* acc_dv, f32x16* acc_dk) {
+  using L = DkdvLds<D>;
+  constexpr int KS = BTile<D>::KS, DB = BTile<D>::DB;
+  constexpr int NS = 2 * KS;    // score slots per half: S and dP over KS k-steps
+  constexpr int NA = 4 * DB;    // dV/dK slots per half: 2 k-blocks x DB column blocks x {dV, dK}
+  static_assert(NS == NA, "the pipeline assumes as many score as dV/dK slots per half");
+  constexpr int NSLOT = 4 * NS;
+  constexpr int VPS = 64 / NSLOT;  // weights formed per slot (32 values over the middle half of the slots)
+  constexpr int V0 = NS + 2;       // slot of the first weight: two slots after the first half's scores
+  constexpr int NF = kLookahead + 1;
+  // Each half's scores are complete before its weights start, and each
+  // k-block of weights is packed before the first dV/dK slot that uses it.
+  static_assert(V0 + 16 / VPS >= 2 * NS + 2, "second half's weights start before its scores end");
+  static_assert(V0 + 7 / VPS < 2 * NS && V0 + 15 / VPS < 2 * NS + 2 * DB, "first half's weights are late");
+  static_assert(V0 + 23 / VPS < 3 * NS && V0 + 31 / VPS < 3 * NS + 2 * DB, "second half's weights are late");
+  const int col = lane & 31, half = lane >> 5;
+
+  // The LDS operand of slot J: Q / dO row fragments for the scores, dO / Q
+  // transposed fragments for dV / dK.
+  auto operand = [&](auto jc) -> u32x4 {
+    constexpr int J = decltype(jc)::value, PH = J / NS, I = J % NS;
+    if constexpr (PH < 2) {
+      return row_frag<D>(slot + ((I & 1) ? L::DO : L::Q), 32 * PH + col, 2 * (I >> 1) + half);
+    } else {
+      constexpr int QM = PH - 2, KK = I / (2 * DB), Q = (I >> 1) % DB;
+      return tr_frag<D>(slot + ((I & 1) ? L::Q : L::DO), Q, 2 * QM + KK, lane);
+    }
+  };
+
   f32x16 sm[2], dp[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm[h][r] = dp[h][r] = 0.f;
   u32x4 pp[2][2], pds[2][2];
-  dkdv_scores<D>(slot, 0, lane, kf, vf, sm[0], dp[0]);
-  dkdv_scores<D>(slot, 1, lane, kf, vf, sm[1], dp[1]);
-  dkdv_weights<D, MASK>(slot, 0, q0, S, my_key, c, lane, sm[0], dp[0], pp[0], pds[0]);
-  dkdv_accumulate<D>(slot, 0, lane, pp[0], pds[0], acc_dv, acc_dk);
-  dkdv_weights<D, MASK>(slot, 1, q0, S, my_key, c, lane, sm[1], dp[1], pp[1], pds[1]);
-  dkdv_accumulate<D>(slot, 1, lane, pp[1], pds[1], acc_dv, acc_dk);
+  // Per half: lse and Dlt of rows qa, qa + 8 for k-blocks 0 and 1.
+  f32x4 lsd[2][4], dsd[2][4];
+  float pv_lo = 0.f, dv_lo = 0.f;
+  u32x4 fr[NF];
+  static_for<0, kLookahead>([&](auto jc) { fr[decltype(jc)::value] = operand(jc); });
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int qa = 32 * h + 16 * kk + 4 * half;
+      lsd[h][2 * kk] = *reinterpret_cast<const f32x4*>(slot + L::LSE + 4 * qa);
+      lsd[h][2 * kk + 1] = *reinterpret_cast<const f32x4*>(slot + L::LSE + 4 * (qa + 8));
+      dsd[h][2 * kk] = *reinterpret_cast<const f32x4*>(slot + L::DLT + 4 * qa);
+      dsd[h][2 * kk + 1] = *reinterpret_cast<const f32x4*>(slot + L::DLT + 4 * (qa + 8));
+    }
+  __builtin_amdgcn_sched_barrier(0);
+
+  static_for<0, NSLOT>([&](auto jc) {
+    constexpr int J = decltype(jc)::value, PH = J / NS, I = J % NS;
+    if constexpr (J + kLookahead < NSLOT)
+      fr[(J + kLookahead) % NF] = operand(std::integral_constant<int, J + kLookahead>{});
+    const u32x4 op = fr[J % NF];
+    if constexpr (PH < 2) {
+      if constexpr (I & 1) dp[PH] = mfma(op, vf[I >> 1], dp[PH]);
+      else sm[PH] = mfma(op, kf[I >> 1], sm[PH]);
+    } else {
+      constexpr int QM = PH - 2, KK = I / (2 * DB), Q = (I >> 1) % DB;
+      if constexpr (I & 1) acc_dk[Q] = mfma(pds[QM][KK], op, acc_dk[Q]);
+      else acc_dv[Q] = mfma(pp[QM][KK], op, acc_dv[Q]);
+    }
+    // VPS weights: values (J - V0) VPS + u of the halves' 2 x 16 score registers.
+    static_for<0, VPS>([&](auto uc) {
+    constexpr int V = (J - V0) * VPS + decltype(uc)::value;
+    if constexpr (V >= 0 && V < 32) {
+      constexpr int H = V / 16, R = V % 16, KK = R / 8, E = (R % 8) / 2, T = R % 2;
+      constexpr int SEL = 2 * KK + ((R >> 2) & 1);
+      const float w = __builtin_amdgcn_exp2f(fmaf(sm[H][R], c, -lsd[H][SEL][R & 3]));
+      float pw = w, dw = w * (dp[H][R] - dsd[H][SEL][R & 3]);
+      if constexpr (MASK) {
+        const int qrow = q0 + 32 * H + 8 * (R >> 2) + 4 * half + (R & 3);
+        const bool live = qrow < S && my_key <= qrow;
+        pw = live ? pw : 0.f;
+        dw = live ? dw : 0.f;
+      }
+      if constexpr (T == 0) {
+        pv_lo = pw;
+        dv_lo = dw;
+      } else {
+        pp[H][KK][E] = pack_bf16x2(pv_lo, pw);
+        pds[H][KK][E] = pack_bf16x2(dv_lo, dw);
+      }
+    }
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
 template <int D>
