@@ -30,7 +30,10 @@
 //    causal mask is applied on diagonal tiles only;
 //  * the running max is only raised (and O rescaled) when a tile's max
 //    exceeds it by more than 2^8, so the rescale is almost never taken; p is
-//    then at most 256, exact in fp32 and within bf16 range;
+//    then at most 256, exact in fp32 and within bf16 range.  The tile max
+//    itself is only computed when some lane's tile sum of p passes 2^8 (a
+//    necessary condition for a p past 2^8): a row block's first tile and the
+//    rare raise -- the common tile does no max reduction at all;
 //  * tiles above a wave's causal diagonal are skipped, workgroups are
 //    issued heaviest q-tile first.
 #include "common.h"
@@ -49,6 +52,7 @@ constexpr int kKT = 64;            // keys per tile
 constexpr int kSlots = 3;          // LDS ring: tile j read, j+1 ready, j+2 written
 constexpr int kXcds = 8;           // MI355X: workgroup i is dispatched to XCD i % 8
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kSumTrigger = 256.0f;      // 2^kRescaleThreshold
 
 // LDS layout: kSlots K tiles, then kSlots V tiles, each row-major
 // [64 keys][D] in 16-byte chunks; chunk c of row r sits at chunk c ^ swz(r).
@@ -177,48 +181,60 @@ __device__ __forceinline__ void compute_tile(WaveCtx<D>& w, int j0) {
         if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
   }
   // ---- online softmax (log2 domain) ----
-  float m0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-  float m1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+  // p = 2^(s*c - m) with the running max m, rounded to bf16 for the PV
+  // product; the row sum adds the same rounded values (packed bf16 dot
+  // products with 1.0), so the numerator and the denominator use identical
+  // weights.
+  u32x4 pf[4];
+  float ps;
+  constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1.0, 1.0)
+  auto probs = [&]() {
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-  for (int r = 3; r < 15; r += 2) {
-    m0 = fmaxf(fmaxf(m0, s[0][r]), s[0][r + 1]);
-    m1 = fmaxf(fmaxf(m1, s[1][r]), s[1][r + 1]);
-  }
-  m0 = fmaxf(fmaxf(m0, s[0][15]), m1);
-  m0 = fmaxf(m0, s[1][15]);
-  const float tmax = max_halves(m0) * w.c;
-  // Raise the running max only when the tile's max exceeds it by more than
-  // the threshold (wave-uniform decision).
-  const bool need = tmax > w.m_run + kRescaleThreshold;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    asm volatile("; rescale" ::);  // keeps this rare path a real branch (no if-conversion)
-    const float m_new = need ? tmax : w.m_run;
-    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);  // 0 on the first tile
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e], w.c, -w.m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e + 1], w.c, -w.m_run));
+        pf[kk][e] = pack_bf16x2(p0, p1);
+        if (e & 1) ps1 = dot2_bf16(pf[kk][e], kOnes, ps1);
+        else ps0 = dot2_bf16(pf[kk][e], kOnes, ps0);
+      }
+    }
+    ps = ps0 + ps1;
+  };
+  probs();
+  // The running max is raised (and O rescaled) only when the tile's max
+  // exceeds it by more than the threshold, i.e. only if some p > 2^8 -- and
+  // then the lane's sum of p exceeds 2^8 as well.  So the tile max is taken
+  // only on tiles where some lane's sum does (a row block's first tile, where
+  // m = -inf gives p = inf; a new max past the threshold; overflow): a rare,
+  // wave-uniform branch that raises m, rescales and recomputes p.
+  if (__builtin_amdgcn_ballot_w64(!(ps <= kSumTrigger))) {
+    float m0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float m1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) {
+      m0 = fmaxf(fmaxf(m0, s[0][r]), s[0][r + 1]);
+      m1 = fmaxf(fmaxf(m1, s[1][r]), s[1][r + 1]);
+    }
+    m0 = fmaxf(fmaxf(m0, s[0][15]), m1);
+    m0 = fmaxf(m0, s[1][15]);
+    const float tmax = max_halves(m0) * w.c;
+    const float m_new = tmax > w.m_run + kRescaleThreshold ? tmax : w.m_run;
+    float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);  // 0 on the first tile
+    // alpha passes through an empty asm, so the multiplications below
+    // cannot be hoisted out of this rare path.
+    asm volatile("; rescale" : "+v"(alpha));
     w.m_run = m_new;
     w.l_run *= alpha;
 #pragma unroll
     for (int q = 0; q < DB; ++q)
 #pragma unroll
       for (int r = 0; r < 16; ++r) w.acc_o[q][r] *= alpha;
+    probs();
   }
-  // p = 2^(s*c - m), rounded to bf16 for the PV product; the row sum adds
-  // the same rounded values (packed bf16 dot products with 1.0), so the
-  // numerator and the denominator use identical weights.
-  u32x4 pf[4];
-  float ps0 = 0.f, ps1 = 0.f;
-  constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1.0, 1.0)
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e], w.c, -w.m_run));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e + 1], w.c, -w.m_run));
-      pf[kk][e] = pack_bf16x2(p0, p1);
-      if (e & 1) ps1 = dot2_bf16(pf[kk][e], kOnes, ps1);
-      else ps0 = dot2_bf16(pf[kk][e], kOnes, ps0);
-    }
-  }
-  w.l_run += ps0 + ps1;
+  w.l_run += ps;
   // ---- O^T += V^T P^T ----
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
