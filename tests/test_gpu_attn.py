@@ -121,6 +121,50 @@ def test_decode_fp32():
     assert_close(o, ref, torch.float32, "decode fp32")
 
 
+def _rising(x, u, step):
+    """Adds step * j * u to row j of x [..., S, D]: scores against queries
+    that point along u grow with the key's position."""
+    S = x.shape[-2]
+    ramp = torch.arange(S, dtype=torch.float64)[:, None] * step * u.double()[None, :]
+    return (x.double() + ramp).to(x.dtype)
+
+
+@pytest.mark.parametrize("dtype,D,growth", [(torch.bfloat16, 128, 8.0), (torch.bfloat16, 64, 8.0),
+                                            (torch.float32, 64, 2.0)])
+def test_prefill_and_decode_when_the_running_max_rises_tile_after_tile(dtype, D, growth):
+    # Keys grow along the sequence in the queries' direction by `growth` (in
+    # units of the scaled score) every 64 keys, so almost every later tile
+    # holds a new row maximum -- for the bf16 kernels, past their rescale
+    # threshold of 2^8 (5.5 score units): the rare raise-and-rescale path
+    # runs on most tiles of most rows, in prefill and in the split-K decode
+    # and its combine.  The fp32 case grows more slowly: scores rounded in
+    # fp32 carry an error of |s| 2^-24, which logits of ~65 would lift past
+    # the 1e-5 bar through the exponentials; at ~16 they stay well inside.
+    B, S, Hq, Hkv = 1, 520, 4, 2
+    g = synth.generator(41 + D)
+    u = synth.normal((D,), g, torch.float64)
+    u = u / u.norm()
+    q = (synth.normal((B, S, Hq, D), g, torch.float64) * 0.3 + 2.0 * u).to(dtype)
+    step = growth / (64 * 2.0 / math.sqrt(D))
+    kc = torch.empty((B, Hkv, S, D), dtype=dtype)
+    vc = synth.normal((B, Hkv, S, D), g, dtype)
+    for h in range(Hkv):
+        kc[0, h] = _rising(synth.normal((S, D), g, dtype), u, step)
+    qs = torch.zeros(B, dtype=torch.int32)
+    ref, ref_lse = oracle.attn(q, kc, vc, qs, want_lse=True)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    o = rgc.gqa_attn_prefill(q.cuda(), kc.cuda(), vc.cuda(), qs.cuda(), lse=lse)
+    assert_close(o, ref, dtype, "prefill, rising scores")
+    lse_tol = LSE_TOL_BF16 if dtype == torch.bfloat16 else 1e-5
+    assert (lse.cpu().double() - ref_lse).abs().max().item() < lse_tol
+    # Decode of the last row over the whole cache.
+    lens = torch.tensor([S], dtype=torch.int32)
+    q1 = q[:, -1].contiguous()
+    ref1 = oracle.attn_decode(q1, kc, vc, lens)
+    o1 = rgc.gqa_attn_decode(q1.cuda(), kc.cuda(), vc.cuda(), lens.cuda(), S)
+    assert_close(o1, ref1, dtype, "decode, rising scores")
+
+
 def test_decode_equals_prefill_last_row_and_gqa_equals_mha_on_gpu():
     # Two GPU-side invariants: the decode row equals the prefill row at the
     # same slot; GQA equals MHA over repeated KV heads.
