@@ -21,67 +21,18 @@
 //    key and P, dS are already the A operand of dV += P^T dO and
 //    dK += dS^T Q; dO and Q enter those as transposed fragments
 //    (ds_read_b64_tr_b16) of the row-major tiles;
-//  * dq_kernel: a workgroup owns 256 query rows of one (sequence, head) (32
-//    per wave) and walks the 64-key tiles at or before them: S^T = K Q^T and
-//    dP^T = V dO^T with queries in the N dimension (Q and dO fragments in
-//    registers), so dS^T is the B operand of dQ^T += K^T dS^T with K^T read
-//    transposed from the K tile.
+//  * dq_kernel (backward_dq.hip): a workgroup owns 128 query rows of one
+//    (sequence, head) and walks the 64-key tiles at or before them.
 // The weights are recomputed from the forward pass's lse; P and dS are
 // rounded to bf16 for the MFMAs, everything accumulates in fp32, and dq, dk,
 // dv are rounded once to bf16.
-#include "common.h"
+#include "bwd_tiles.h"
 #include "launch.h"
-#include "mfma_attn.h"
 
 namespace rgc {
 namespace {
 
-// Row-major bf16 tiles in LDS with 16-byte chunk c of row r stored at chunk
-// c ^ swz(r).  With 64 four-byte banks (256 bytes), a 16-byte row fragment
-// read covers 16 consecutive rows at one chunk, and a transposed fragment
-// read (8 bytes a lane, 32 lanes at a time) covers 4 consecutive rows at 4
-// consecutive chunks of an aligned group of 4.  swz is a bijection of the
-// row's position among the rows that share a 256-byte bank line (so the
-// first read meets every bank once), and it sends the 4 rows of the second
-// read to different 4-chunk groups when they share a line (D = 128: one row
-// per line; D = 64: two).
-template <int D>
-struct BTile {
-  static constexpr int CH = D / 8;
-  static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
-  static constexpr int ROW_BYTES = D * 2;
-  static __device__ __forceinline__ int swz(int r) {
-    if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    if (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-    return (r >> 2) & 3;
-  }
-  static __device__ __forceinline__ int phys(int r, int c) { return r * ROW_BYTES + 16 * (c ^ swz(r)); }
-};
-
-// 16-byte row fragment: row r, logical chunk c.
-template <int D>
-__device__ __forceinline__ u32x4 row_frag(const char* tile, int r, int c) {
-  return *reinterpret_cast<const u32x4*>(tile + BTile<D>::phys(r, c));
-}
-
-// Transposed fragment of rows 16kk .. 16kk+15 and columns 32q .. 32q+31 of a
-// row-major tile: lane j gets, at column 32q + j%32, the values of rows
-// 16kk + 4h + (0..3) and 16kk + 8 + 4h + (0..3), h = j/32 -- the MFMA operand
-// layout whose k index runs over rows (see vt_frag).
-template <int D>
-__device__ __forceinline__ u32x4 tr_frag(const char* tile, int q, int kk, int lane) {
-  const int x = lane & 15, beta = (lane >> 4) & 1, h = lane >> 5;
-  const int c_lane = 2 * beta + ((x & 3) >> 1);  // 4-column group inside the 32-column block
-  const int r = 16 * kk + 4 * h + (x >> 2);
-  const int c = 4 * q + c_lane;                   // logical 8-byte-pair chunk
-  const char* lo = tile + BTile<D>::phys(r, c) + 8 * (x & 1);
-  const char* hi = tile + BTile<D>::phys(r + 8, c) + 8 * (x & 1);
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
-  const u32x2 a2 = __builtin_bit_cast(u32x2, a), b2 = __builtin_bit_cast(u32x2, b);
-  return u32x4{a2[0], a2[1], b2[0], b2[1]};
-}
+using namespace bwd;
 
 // Cooperative copy of `rows` rows (row stride `gstride` elements) from HBM
 // into a swizzled LDS tile; rows at or past `valid` are filled with zeros.
@@ -124,38 +75,6 @@ __global__ void __launch_bounds__(256) delta_kernel(BwdParams p, float* dlt) {
   for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m, 64);
   if (row < nrows && sub == 0) dlt[row] = acc;
 }
-
-// ---------------------------------------------------------------------------
-// A thread's share of a rows x D tile, fetched into registers ahead of use
-// and stored into a swizzled LDS tile after the current step's arithmetic.
-// The loads are unconditional (rows past `valid` re-read row valid - 1) so
-// that nothing waits for them before the store; the store writes zeros for
-// those rows.  Row offsets are 32-bit byte offsets from a uniform base (the
-// host keeps the row stride below 2^24 elements).
-template <int D, int ROWS, int NT>
-struct TileRegs {
-  static constexpr int CHUNKS = ROWS * BTile<D>::CH;
-  static constexpr int N = (CHUNKS + NT - 1) / NT;  // 16-byte chunks per thread
-  static_assert(CHUNKS % NT == 0 || CHUNKS < NT, "tile chunks must split evenly over the threads");
-  u32x4 r[N];
-  __device__ __forceinline__ void fetch(const char* g, uint32_t row_bytes, int valid, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = min(tid + i * NT, CHUNKS - 1), c = idx % BTile<D>::CH;
-      const uint32_t row = (uint32_t)min(idx / BTile<D>::CH, valid - 1);
-      r[i] = ld16(g + (row * row_bytes + 16u * (uint32_t)c));
-    }
-  }
-  __device__ __forceinline__ void store(char* tile, int valid, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + i * NT, row = idx / BTile<D>::CH, c = idx % BTile<D>::CH;
-      const u32x4 z{0, 0, 0, 0};
-      if (CHUNKS % NT == 0 || idx < CHUNKS)
-        *reinterpret_cast<u32x4*>(tile + BTile<D>::phys(row, c)) = row < valid ? r[i] : z;
-    }
-  }
-};
 
 constexpr int kKeysPerWave = 32;
 constexpr int kDkdvWaves = 4;
@@ -232,15 +151,6 @@ __device__ __forceinline__ void store_step(const StepRegs<D>& st, char* slot, in
 // MASK zeroes the pairs with query < key and rows past S; steps where every
 // pair is live skip it.
 constexpr int kLookahead = 3;
-
-// Compile-time loop: f(std::integral_constant<int, J>) for J = B .. E - 1.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
 
 template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_step(const char* slot, int q0, int S, int my_key, float c, int lane,
@@ -424,171 +334,6 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) dkdv_kernel(BwdParams p, cons
     }
 }
 
-// ---------------------------------------------------------------------------
-constexpr int kDqWaves = 4;
-constexpr int kDqThreads = 64 * kDqWaves;
-constexpr int kDqRows = 32 * kDqWaves;  // 128 query rows per workgroup
-constexpr int kKT = 64;                 // keys per tile
-
-// Two slots of (K, V) key tiles: the current one and the next, which is
-// fetched into registers during the current tile's arithmetic.
-template <int D>
-struct DqLds {
-  static constexpr int K = 0;                   // slot-relative: [64][D]
-  static constexpr int V = K + kKT * D * 2;     // [64][D]
-  static constexpr int SLOT_BYTES = V + kKT * D * 2;
-  static constexpr int BYTES = 2 * SLOT_BYTES;
-};
-
-template <int D>
-struct KvRegs {
-  TileRegs<D, kKT, kDqThreads> k, v;
-  int valid;
-};
-
-// One 32-key half (kb) of a key tile for one wave: S^T = K Q^T and
-// dP^T = V dO^T with the wave's 32 queries in the MFMA N dimension (lane
-// holds query qi; register r holds key j0 + 32kb + 8(r/4) + 4half + r%4),
-// dS^T = P^T (dP^T - Dlt) rounded to bf16 in the B-operand layout of
-// dQ^T += K^T dS^T, with K^T read transposed from the K tile.  MASK zeroes
-// the pairs with key > query and rows past S; tiles where every pair is
-// live skip it.
-template <int D, bool MASK>
-__device__ __forceinline__ void dq_unit(const char* slot, int kb, int j0, int qi, bool qvalid, float lse2, float dl,
-                                        float c, int lane, const u32x4* qf, const u32x4* dof, f32x16* acc) {
-  using L = DqLds<D>;
-  constexpr int KS = BTile<D>::KS, DB = BTile<D>::DB;
-  const int col = lane & 31, half = lane >> 5;
-  f32x16 sm, dp;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sm[r] = dp[r] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    sm = mfma(row_frag<D>(slot + L::K, 32 * kb + col, 2 * ks + half), qf[ks], sm);
-    dp = mfma(row_frag<D>(slot + L::V, 32 * kb + col, 2 * ks + half), dof[ks], dp);
-  }
-  u32x4 pf[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float v2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = 8 * kk + 2 * e + u;
-        const float w = __builtin_amdgcn_exp2f(fmaf(sm[r], c, -lse2));
-        if (MASK) {
-          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          v2[u] = qvalid && key <= qi ? w * (dp[r] - dl) : 0.f;
-        } else {
-          v2[u] = w * (dp[r] - dl);
-        }
-      }
-      pf[kk][e] = pack_bf16x2(v2[0], v2[1]);
-    }
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int q = 0; q < DB; ++q) acc[q] = mfma(tr_frag<D>(slot + L::K, q, 2 * kb + kk, lane), pf[kk], acc[q]);
-}
-
-template <int D>
-__global__ void __launch_bounds__(kDqThreads, 1) dq_kernel(BwdParams p, const float* dlt) {
-  using T = BTile<D>;
-  using L = DqLds<D>;
-  constexpr int KS = T::KS, DB = T::DB;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int nqt = (p.S + kDqRows - 1) / kDqRows;
-  const int qt = nqt - 1 - (int)(blockIdx.x / (p.B * p.Hq));  // heaviest tiles first
-  const int h = blockIdx.x % p.Hq;
-  const int b = (blockIdx.x / p.Hq) % p.B;
-  const int kvh = h / (p.Hq / p.Hkv);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 31, half = lane >> 5;
-  const float c = p.scale * kAttnLog2e;
-
-  const int s_base = qt * kDqRows + wave * 32;
-  const int qi = s_base + col;  // this lane's query row
-  const bool qvalid = qi < p.S;
-  const int64_t qoff = (int64_t)b * p.q_sb + (int64_t)qi * p.q_ss + (int64_t)h * p.q_sh;
-  u32x4 qf[KS], dof[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = qvalid ? ld16(reinterpret_cast<const bf16_t*>(p.q) + qoff + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
-    dof[ks] = qvalid ? ld16(reinterpret_cast<const bf16_t*>(p.dO) + qoff + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
-  }
-  const float lse2 = qvalid ? p.lse[((int64_t)b * p.Hq + h) * p.S + qi] * kAttnLog2e : 0.f;
-  const float dl = qvalid ? dlt[((int64_t)b * p.Hq + h) * p.S + qi] : 0.f;
-
-  f32x16 acc[DB];
-#pragma unroll
-  for (int q = 0; q < DB; ++q)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
-
-  const int last_row = min(p.S, (qt + 1) * kDqRows) - 1;  // the workgroup's last query
-  const int nkt = last_row / kKT + 1;
-  const int wave_last = s_base < p.S ? min(s_base + 31, p.S - 1) : -1;
-  const bool rows_full = s_base + 31 < p.S;
-  const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.kv_sb +
-                                                 (int64_t)kvh * p.kv_sh);
-  const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.kv_sb +
-                                                 (int64_t)kvh * p.kv_sh);
-  const uint32_t row_bytes = (uint32_t)p.kv_ss * 2u;
-  KvRegs<D> st;
-  auto fetch = [&](int j0) {
-    st.valid = min(kKT, p.S - j0);
-    const int64_t off = (int64_t)j0 * p.kv_ss * 2;
-    st.k.fetch(kg + off, row_bytes, st.valid, tid);
-    st.v.fetch(vg + off, row_bytes, st.valid, tid);
-  };
-  auto store = [&](char* slot) {
-    st.k.store(slot + L::K, st.valid, tid);
-    st.v.store(slot + L::V, st.valid, tid);
-  };
-  fetch(0);
-  store(lds);
-  __syncthreads();
-  // Key tiles alternate between the two slots, two per iteration, so that
-  // slot addresses are compile-time offsets.
-  auto step = [&](auto slot_tag, int t) {
-    constexpr int SL = decltype(slot_tag)::value;
-    const int j0 = t * kKT;
-    const bool more = t + 1 < nkt;
-    if (more) fetch(j0 + kKT);
-    const char* slot = lds + SL * L::SLOT_BYTES;
-    if (wave_last >= j0) {
-      if (j0 + kKT - 1 <= s_base && rows_full) {  // every pair of the tile is live
-        dq_unit<D, false>(slot, 0, j0, qi, qvalid, lse2, dl, c, lane, qf, dof, acc);
-        dq_unit<D, false>(slot, 1, j0, qi, qvalid, lse2, dl, c, lane, qf, dof, acc);
-      } else {
-        dq_unit<D, true>(slot, 0, j0, qi, qvalid, lse2, dl, c, lane, qf, dof, acc);
-        dq_unit<D, true>(slot, 1, j0, qi, qvalid, lse2, dl, c, lane, qf, dof, acc);
-      }
-    }
-    if (more) store(lds + (SL ^ 1) * L::SLOT_BYTES);
-    __syncthreads();
-  };
-  for (int t = 0; t < nkt; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < nkt) step(std::integral_constant<int, 1>{}, t + 1);
-  }
-  // acc[q] register r holds d = 32q + 8(r/4) + 4half + r%4 of query qi.
-  if (qvalid) {
-    bf16_t* dqr = reinterpret_cast<bf16_t*>(p.dq) + qoff;
-#pragma unroll
-    for (int q = 0; q < DB; ++q)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * q + 8 * q4 + 4 * half;
-        u32x2 wv;
-        wv[0] = pack_bf16x2(acc[q][4 * q4] * p.scale, acc[q][4 * q4 + 1] * p.scale);
-        wv[1] = pack_bf16x2(acc[q][4 * q4 + 2] * p.scale, acc[q][4 * q4 + 3] * p.scale);
-        *reinterpret_cast<u32x2*>(dqr + d) = wv;
-      }
-  }
-}
-
 template <int D>
 hipError_t launch_d(const BwdParams& p, float* dlt, hipStream_t stream) {
   const int nkb = (p.S + kKeyBlock - 1) / kKeyBlock;
@@ -596,10 +341,7 @@ hipError_t launch_d(const BwdParams& p, float* dlt, hipStream_t stream) {
                      (size_t)DkdvLds<D>::BYTES, stream, p, (const float*)dlt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nqt = (p.S + kDqRows - 1) / kDqRows;
-  hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(p.B * p.Hq * nqt)), dim3(kDqThreads), (size_t)DqLds<D>::BYTES,
-                     stream, p, (const float*)dlt);
-  return hipGetLastError();
+  return launch_dq_bf16(p, dlt, stream);
 }
 
 }  // namespace
