@@ -63,7 +63,8 @@ typedef enum {
   RGC_ERR_NULL = -1,      /* a required pointer is NULL                      */
   RGC_ERR_SHAPE = -2,     /* a negative or inconsistent size                 */
   RGC_ERR_GROUP = -3,     /* Hq is not a multiple of Hkv                     */
-  RGC_ERR_DTYPE = -4,     /* dtype is neither RGC_F32 nor RGC_BF16           */
+  RGC_ERR_DTYPE = -4,     /* dtype is not RGC_F32 or RGC_BF16, or not one    */
+                          /* the call supports                               */
   RGC_ERR_HEADDIM = -5,   /* head dim not supported                          */
   RGC_ERR_LAYOUT = -6,    /* misaligned pointer or stride                    */
   RGC_ERR_CAPACITY = -7,  /* a host-known length exceeds the cache           */
@@ -322,6 +323,41 @@ int rgc_gqa_attn_decode(void* o, const void* q, const void* k_cache,
                         int max_len, float scale, void* workspace,
                         size_t ws_bytes, float* lse, int32_t* err_flag,
                         void* stream);
+
+/*
+ * rgc_gqa_attn_decode_rope_append -- one whole cached-generation step for
+ * one new token per sequence: RoPE on its q and k at its position, the
+ * append of its k and v to the caches, and its attention over the cache, in
+ * one decode launch (plus the chunk merge) instead of a prologue launch
+ * before the decode (the first page's section V3 describes the step).
+ *   o         [B,Hq,D] bf16, strides (o_sb, o_sh); written.
+ *   q         [B,Hq,D] bf16, strides (q_sb, q_sh); NOT rotated, and left
+ *             unrotated (read only).
+ *   k_new, v_new  [B,Hkv,D] bf16, strides (n_sb, n_sh) shared by both;
+ *             read only.
+ *   k_cache, v_cache  [B,Hkv,S_max,D] bf16, strides (kv_sb, kv_sh, kv_ss):
+ *             slot seq_lens[b] - 1 of each receives the rotated k_new and
+ *             v_new; the other slots are read only.
+ *   seq_lens  [B] int32: cache length INCLUDING the new token, whose
+ *             position and slot is seq_lens[b] - 1.
+ *   base, style  as rgc_rope_apply; max_len, scale, workspace, ws_bytes,
+ *             lse as rgc_gqa_attn_decode.
+ * o, lse and the caches are bit for bit those of rgc_rope_append (S = 1,
+ * pos0 = seq_lens - 1) followed by rgc_gqa_attn_decode of the rotated q; the
+ * only difference is that q itself is not rotated in place.  bf16 only
+ * (RGC_ERR_DTYPE otherwise).  A sequence whose seq_lens is outside
+ * [1, min(max_len, S_max)] gets NaN rows and the flag, and its cache is not
+ * written.  Calls that overlap in time must use different workspaces.
+ */
+int rgc_gqa_attn_decode_rope_append(void* o, const void* q, const void* k_new,
+                                    const void* v_new, void* k_cache, void* v_cache,
+                                    int dtype, int B, int Hq, int Hkv, int D, int S_max,
+                                    int64_t q_sb, int64_t q_sh, int64_t n_sb, int64_t n_sh,
+                                    int64_t o_sb, int64_t o_sh, int64_t kv_sb,
+                                    int64_t kv_sh, int64_t kv_ss, const int32_t* seq_lens,
+                                    int max_len, double base, int style, float scale,
+                                    void* workspace, size_t ws_bytes, float* lse,
+                                    int32_t* err_flag, void* stream);
 
 #ifdef __cplusplus
 }

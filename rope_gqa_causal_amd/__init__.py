@@ -66,6 +66,9 @@ _SIGNATURES = {
     "rgc_gqa_attn_decode": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                  _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                  _p, _i, _f, _p, _sz, _p, _p, _p]),
+    "rgc_gqa_attn_decode_rope_append": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                             _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                             _p, _i, _d, _i, _f, _p, _sz, _p, _p, _p]),
 }
 
 _lib = None
@@ -314,6 +317,39 @@ def decode_workspace(B, Hq, Hkv, D, max_len, device="cuda"):
     """A zero-filled workspace tensor large enough for gqa_attn_decode."""
     n = max(gqa_attn_decode_workspace_size(B, Hq, Hkv, D, max_len), 256)
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def gqa_attn_decode_rope_append(q, k_new, v_new, k_cache, v_cache, seq_lens, max_len=None, workspace=None,
+                                base=10000.0, style=ROPE_HALF, scale=None, out=None, lse=None, err_flag=None):
+    """One generation step in one decode launch: q [B,Hq,D] and k_new [B,Hkv,D] turned at
+    position seq_lens[b]-1, k_new (rotated) and v_new [B,Hkv,D] written to that cache slot,
+    and the attention of q over slots 0..seq_lens[b]-1.  q is left unrotated; bf16 only."""
+    _gpu(q, k_new, v_new, k_cache, v_cache, seq_lens, workspace, out, lse, err_flag)
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    if v_cache.stride() != k_cache.stride():
+        raise ValueError("k_cache and v_cache must share strides")
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D) or k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must be [B,Hkv,D] with one set of strides")
+    if k_new.stride(2) != 1 or q.stride(2) != 1:
+        raise ValueError("q, k_new and v_new need unit stride along D")
+    if scale is None:
+        scale = D ** -0.5
+    if max_len is None:
+        max_len = S_max
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, Hkv, D, max_len, q.device)
+    o = torch.empty_like(q) if out is None else out
+    seq_lens = _lens(seq_lens, B, "seq_lens")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq)):
+        raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
+    _call("rgc_gqa_attn_decode_rope_append", _ptr(o), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+          _ptr(v_cache), _dtype(q), B, Hq, Hkv, D, S_max, q.stride(0), q.stride(1), k_new.stride(0),
+          k_new.stride(1), o.stride(0), o.stride(1), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+          _ptr(seq_lens), int(max_len), float(base), int(style), float(scale), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _ptr(lse), _ptr(err_flag), _stream(q))
+    return o
 
 
 def gqa_attn_decode(q, k_cache, v_cache, seq_lens, max_len=None, workspace=None, scale=None,

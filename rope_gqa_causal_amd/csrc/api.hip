@@ -467,4 +467,65 @@ int rgc_gqa_attn_decode(void* o, const void* q, const void* k_cache, const void*
   return hip_status(launch_decode_bf16(p, workspace, s));
 }
 
+int rgc_gqa_attn_decode_rope_append(void* o, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                    void* v_cache, int dtype, int B, int Hq, int Hkv, int D, int S_max,
+                                    int64_t q_sb, int64_t q_sh, int64_t n_sb, int64_t n_sh, int64_t o_sb,
+                                    int64_t o_sh, int64_t kv_sb, int64_t kv_sh, int64_t kv_ss,
+                                    const int32_t* seq_lens, int max_len, double base, int style, float scale,
+                                    void* workspace, size_t ws_bytes, float* lse, int32_t* err_flag,
+                                    void* stream) {
+  int st = check_attn_common(dtype, B, 1, Hq, Hkv, D, S_max);
+  if (st != RGC_OK) return st;
+  if (dtype != RGC_BF16) return RGC_ERR_DTYPE;
+  if (style != RGC_ROPE_HALF && style != RGC_ROPE_INTERLEAVED) return RGC_ERR_ARG;
+  if (!(base > 0.0) || !std::isfinite(base)) return RGC_ERR_ARG;
+  if (B == 0) return RGC_OK;
+  if (!o || !q || !k_new || !v_new || !k_cache || !v_cache || !seq_lens) return RGC_ERR_NULL;
+  if (max_len < 1 || max_len > S_max) return RGC_ERR_CAPACITY;
+  if (!std::isfinite(scale)) return RGC_ERR_ARG;
+  if (!aligned16(o) || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return RGC_ERR_LAYOUT;
+  if (!stride_ok(q_sb, dtype) || !stride_ok(q_sh, dtype) || !stride_ok(n_sb, dtype) || !stride_ok(n_sh, dtype) ||
+      !stride_ok(o_sb, dtype) || !stride_ok(o_sh, dtype) || !stride_ok(kv_sb, dtype) ||
+      !stride_ok(kv_sh, dtype) || !stride_ok(kv_ss, dtype))
+    return RGC_ERR_LAYOUT;
+  const size_t need = decode_workspace_bytes(B, Hq, Hkv, D, max_len);
+  if (!workspace || ws_bytes < need) return RGC_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RGC_ERR_LAYOUT;
+  AttnParams p = {};
+  p.o = o;
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.B = B;
+  p.Sq = 1;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.S_max = S_max;
+  p.q_sb = q_sb;
+  p.q_sh = q_sh;
+  p.o_sb = o_sb;
+  p.o_sh = o_sh;
+  p.kv_sb = kv_sb;
+  p.kv_sh = kv_sh;
+  p.kv_ss = kv_ss;
+  p.seq_lens = seq_lens;
+  p.max_len = max_len;
+  p.scale = scale;
+  p.lse = lse;
+  p.err = err_flag;
+  DecodeRope r = {};
+  r.k_new = k_new;
+  r.v_new = v_new;
+  r.k_cache = k_cache;
+  r.v_cache = v_cache;
+  r.n_sb = n_sb;
+  r.n_sh = n_sh;
+  r.style = style;
+  for (int i = 0; i < 64; ++i) r.theta[i] = i < D / 2 ? std::pow(base, -2.0 * (double)i / (double)D) : 0.0;
+  return hip_status(launch_decode_rope_bf16(p, r, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -35,6 +35,7 @@
 //    invalidates the XCD's L2: measured 16x slower than the second launch.)
 #include "common.h"
 #include "launch.h"
+#include "rope_math.h"
 
 namespace rgc {
 namespace {
@@ -109,9 +110,15 @@ __device__ __forceinline__ bool len_ok(const AttnParams& p, int L) {
 }
 
 // D: head dim; GS: query heads per workgroup (all of them share KV head kvh);
-// MUL: keys per wave in units of one q.k pass.
-template <int D, int GS, int MUL>
-__global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p, DecodeWs ws, int nsub) {
+// MUL: keys per wave in units of one q.k pass.  ROPE: the new token's RoPE
+// and append happen here (DecodeRope): every workgroup turns its q rows at
+// position L - 1; the sequence's last chunk, the only one that holds slot
+// L - 1, takes the new token's rotated k and its v from registers instead
+// of the cache, and its first head subgroup writes them into the caches (no
+// workgroup reads that slot from memory, so the write races with nothing).
+template <int D, int GS, int MUL, bool ROPE>
+__global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p, DecodeWs ws, int nsub,
+                                                                   DecodeRope r) {
   constexpr int WK = Chunk<D, MUL>::WAVE_KEYS;
   constexpr int LPK = D / 32;      // lanes per key in the q.k layout
   constexpr int KPP = 64 / LPK;    // keys per pass
@@ -168,17 +175,40 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
   const bool active = kw < L;  // wave-uniform
   const int part = lane % LPK, key_sub = lane / LPK;
   const int dgrp = lane % LPR, kq = lane / LPR;
+  const bool last = split == ns - 1;  // the chunk that holds slot L - 1
   if (active) {
     // ---- issue every load of the wave's keys (q first: the scores need it
     // before the values).  Keys past the end re-read the last row, which
     // keeps every load unconditional and in bounds; their scores are masked
     // to -inf, so they weigh nothing.
     u32x4 qf[GS][4];
+    // With ROPE, lane m < D/2 instead loads pair m (elements ia, ib) of each
+    // q row and, in the last chunk, of the new k; it turns them below and
+    // the rows reach the q.k layout through LDS.
+    constexpr int HALF = D / 2;
+    const int ia = r.style == ROPE_HALF ? lane : 2 * lane, ib = r.style == ROPE_HALF ? lane + HALF : 2 * lane + 1;
+    float pa[GS + 1], pb[GS + 1];
+    if constexpr (ROPE) {
+      if (lane < HALF) {
 #pragma unroll
-    for (int g = 0; g < GS; ++g) {
-      const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
+        for (int g = 0; g < GS; ++g) {
+          const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
+          pa[g] = bf16_to_f32(qr[ia]);
+          pb[g] = bf16_to_f32(qr[ib]);
+        }
+        if (last) {
+          const bf16_t* knr = reinterpret_cast<const bf16_t*>(r.k_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh;
+          pa[GS] = bf16_to_f32(knr[ia]);
+          pb[GS] = bf16_to_f32(knr[ib]);
+        }
+      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qf[g][i] = ld16(qr + 8 * (part + LPK * i));
+      for (int g = 0; g < GS; ++g) {
+        const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qf[g][i] = ld16(qr + 8 * (part + LPK * i));
+      }
     }
     u32x4 kf[PASSES][4], vf[VLOADS];
 #pragma unroll
@@ -193,7 +223,63 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
       const int key = min(kw + t * KPI + kq, L - 1);
       vf[t] = ld16(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
     }
+    u32x4 kn[4] = {}, vn = {};  // the new token's rotated k and its v (last chunk)
+    if constexpr (ROPE) {
+      if (last)
+        vn = ld16(reinterpret_cast<const bf16_t*>(r.v_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh + 8 * dgrp);
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
+
+    if constexpr (ROPE) {
+      // Pair m = lane turns by (L - 1) theta_m (same angle, rotation and
+      // rounding as the RoPE kernels); the rotated rows go through this
+      // wave's LDS rows into the q.k layout.
+      __shared__ __attribute__((aligned(16))) bf16_t rows[kWaves][GS + 1][D];
+      if (lane < HALF) {
+        float sn, cs;
+        angle_sincos((double)(L - 1) * r.theta[lane], &sn, &cs);
+#pragma unroll
+        for (int g = 0; g <= GS; ++g) {
+          if (g == GS && !last) break;
+          float ra, rb;
+          rope_rotate_pair(pa[g], pb[g], sn, cs, ra, rb);
+          rows[wave][g][ia] = f32_to_bf16(ra);
+          rows[wave][g][ib] = f32_to_bf16(rb);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's rows landed
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qf[g][i] = *reinterpret_cast<const u32x4*>(&rows[wave][g][8 * (part + LPK * i)]);
+      if (last) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kn[i] = *reinterpret_cast<const u32x4*>(&rows[wave][GS][8 * (part + LPK * i)]);
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps)
+          if (min(kw + ps * KPP + key_sub, L - 1) == L - 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kf[ps][i] = kn[i];
+#pragma unroll
+        for (int t = 0; t < VLOADS; ++t)
+          if (min(kw + t * KPI + kq, L - 1) == L - 1) vf[t] = vn;
+        if (hs == 0) {
+          bf16_t* kc = reinterpret_cast<bf16_t*>(r.k_cache) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh +
+                       (int64_t)(L - 1) * p.kv_ss;
+          bf16_t* vc = reinterpret_cast<bf16_t*>(r.v_cache) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh +
+                       (int64_t)(L - 1) * p.kv_ss;
+#pragma unroll
+          for (int ps = 0; ps < PASSES; ++ps)
+            if (kw + ps * KPP + key_sub == L - 1)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) st16(kc + 8 * (part + LPK * i), kn[i]);
+#pragma unroll
+          for (int t = 0; t < VLOADS; ++t)
+            if (kw + t * KPI + kq == L - 1) st16(vc + 8 * dgrp, vn);
+        }
+      }
+    }
 
     // ---- scores: z = scale * log2(e) * q.k ----
     float z[GS][PASSES];
@@ -371,14 +457,16 @@ int heads_per_wg(int group) {
   return 1;
 }
 
-template <int D, int MUL>
-hipError_t launch_dm(const AttnParams& p, DecodeWs ws, int gs, int nsub, hipStream_t stream) {
+template <int D, int MUL, bool ROPE>
+hipError_t launch_dm(const AttnParams& p, const DecodeRope& r, DecodeWs ws, int gs, int nsub, hipStream_t stream) {
   const dim3 grid(ws.NS, p.Hkv * nsub, p.B), block(64 * kWaves);
   switch (gs) {
-    case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, MUL>), grid, block, 0, stream, p, ws, nsub); break;
-    case 3: hipLaunchKernelGGL((decode_split_kernel<D, 3, MUL>), grid, block, 0, stream, p, ws, nsub); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, MUL>), grid, block, 0, stream, p, ws, nsub); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<D, 1, MUL>), grid, block, 0, stream, p, ws, nsub); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, MUL, ROPE>), grid, block, 0, stream, p, ws, nsub, r); break;
+    case 3: hipLaunchKernelGGL((decode_split_kernel<D, 3, MUL, ROPE>), grid, block, 0, stream, p, ws, nsub, r); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, MUL, ROPE>), grid, block, 0, stream, p, ws, nsub, r); break;
+    default:
+      hipLaunchKernelGGL((decode_split_kernel<D, 1, MUL, ROPE>), grid, block, 0, stream, p, ws, nsub, r);
+      break;
   }
   return hipGetLastError();
 }
@@ -391,15 +479,16 @@ int chunk_mul(int B, int Hkv, int nsub, int D, int max_len) {
   return wgs >= 4 * 256 ? 2 : 1;
 }
 
-template <int D>
-hipError_t launch_d(const AttnParams& p, DecodeWs ws, hipStream_t stream) {
+template <int D, bool ROPE>
+hipError_t launch_d(const AttnParams& p, const DecodeRope& r, DecodeWs ws, hipStream_t stream) {
   const int group = p.Hq / p.Hkv;
   const int gs = heads_per_wg(group);
   const int nsub = group / gs;
   const int mul = chunk_mul(p.B, p.Hkv, nsub, D, p.max_len);
   ws.chunk = chunk_keys(D, mul);
   ws.NS = (p.max_len + ws.chunk - 1) / ws.chunk;
-  hipError_t e = mul == 2 ? launch_dm<D, 2>(p, ws, gs, nsub, stream) : launch_dm<D, 1>(p, ws, gs, nsub, stream);
+  hipError_t e = mul == 2 ? launch_dm<D, 2, ROPE>(p, r, ws, gs, nsub, stream)
+                          : launch_dm<D, 1, ROPE>(p, r, ws, gs, nsub, stream);
   if (e != hipSuccess || ws.NS <= 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((p.B * p.Hq + 3) / 4), dim3(256), 0, stream, p, ws);
   return hipGetLastError();
@@ -426,7 +515,10 @@ size_t decode_workspace_bytes(int B, int Hq, int /*Hkv*/, int D, int max_len) {
   return l.o_bytes + l.ml_bytes;
 }
 
-hipError_t launch_decode_bf16(const AttnParams& p, void* workspace, hipStream_t stream) {
+namespace {
+
+template <bool ROPE>
+hipError_t launch_decode(const AttnParams& p, const DecodeRope& r, void* workspace, hipStream_t stream) {
   const WsLayout l = ws_layout(p.B, p.Hq, p.D, p.max_len);
   DecodeWs ws;
   ws.NS = 0;     // set with the chunk length at launch
@@ -435,10 +527,20 @@ hipError_t launch_decode_bf16(const AttnParams& p, void* workspace, hipStream_t 
   ws.part_o = reinterpret_cast<float*>(base);
   ws.part_ml = reinterpret_cast<float*>(base + l.o_bytes);
   switch (p.D) {
-    case 32: return launch_d<32>(p, ws, stream);
-    case 64: return launch_d<64>(p, ws, stream);
-    default: return launch_d<128>(p, ws, stream);
+    case 32: return launch_d<32, ROPE>(p, r, ws, stream);
+    case 64: return launch_d<64, ROPE>(p, r, ws, stream);
+    default: return launch_d<128, ROPE>(p, r, ws, stream);
   }
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const AttnParams& p, void* workspace, hipStream_t stream) {
+  return launch_decode<false>(p, DecodeRope{}, workspace, stream);
+}
+
+hipError_t launch_decode_rope_bf16(const AttnParams& p, const DecodeRope& r, void* workspace, hipStream_t stream) {
+  return launch_decode<true>(p, r, workspace, stream);
 }
 
 }  // namespace rgc

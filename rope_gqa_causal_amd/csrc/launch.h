@@ -113,4 +113,19 @@ hipError_t launch_dq_bf16(const BwdParams& p, const float* dlt, hipStream_t stre
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len);
 hipError_t launch_decode_bf16(const AttnParams& p, void* ws, hipStream_t stream);
 
+// The new token's RoPE and cache append, done by the decode itself: q (read
+// from AttnParams::q, left unrotated) and k_new are turned at position
+// seq_lens[b] - 1, and the rotated k and v_new are written into the caches
+// at that slot.
+struct DecodeRope {
+  const void* k_new;   // [B,Hkv,D] of bf16, strides (n_sb, n_sh)
+  const void* v_new;
+  void* k_cache;       // the caches of AttnParams, writable
+  void* v_cache;
+  int64_t n_sb, n_sh;
+  int style;           // ROPE_HALF or ROPE_INTERLEAVED
+  double theta[64];    // base^(-2i/D) for i < D/2, formed on the host in fp64
+};
+hipError_t launch_decode_rope_bf16(const AttnParams& p, const DecodeRope& r, void* ws, hipStream_t stream);
+
 }  // namespace rgc

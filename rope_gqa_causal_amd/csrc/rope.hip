@@ -15,26 +15,13 @@
 // still spreads over many threads.
 #include "common.h"
 #include "launch.h"
+#include "rope_math.h"
 
 namespace rgc {
 namespace {
 
 constexpr int kBlock = 256;
 constexpr int kTableFloats = 1024;  // sin (and cos) entries per workgroup
-
-// sin and cos of a (possibly large) angle in radians.  The product
-// position * theta and the reduction to [-pi, pi] run in fp64 with 2*pi
-// split into a double and its rounding error, so the reduced angle is good
-// to ~1e-16 absolute for any int32 position; fp32 sincosf then adds ~1 ulp.
-__device__ __forceinline__ void angle_sincos(double ang, float* s, float* c) {
-  const double kInv2Pi = 0.15915494309189535;
-  const double k2PiHi = 6.283185307179586;          // nearest double to 2*pi
-  const double k2PiLo = 2.4492935982947064e-16;     // 2*pi - k2PiHi
-  double n = rint(ang * kInv2Pi);
-  double r = fma(-n, k2PiHi, ang);
-  r = fma(-n, k2PiLo, r);
-  sincosf((float)r, s, c);
-}
 
 template <typename T>
 struct Elem;
@@ -113,8 +100,8 @@ struct Chunk {
     float w0[E], w1[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const float ra = fmaf(a[e], cs[e], -bb[e] * sn[e]);
-      const float rb = fmaf(a[e], sn[e], bb[e] * cs[e]);
+      float ra, rb;
+      rope_rotate_pair(a[e], bb[e], sn[e], cs[e], ra, rb);
       if (STYLE == ROPE_HALF) {
         w0[e] = ra;
         w1[e] = rb;
@@ -197,9 +184,10 @@ __global__ void __launch_bounds__(256) rope_scalar_kernel(RopeParams p) {
   T* base = reinterpret_cast<T*>(p.x) + (int64_t)b * p.sb + (int64_t)s * p.ss;
   for (int h = 0; h < p.H; ++h) {
     T* row = base + (int64_t)h * p.sh;
-    float a = Elem<T>::load1(row + ia), bb = Elem<T>::load1(row + ib);
-    Elem<T>::store1(row + ia, fmaf(a, cs, -bb * sn));
-    Elem<T>::store1(row + ib, fmaf(a, sn, bb * cs));
+    float a = Elem<T>::load1(row + ia), bb = Elem<T>::load1(row + ib), ra, rb;
+    rope_rotate_pair(a, bb, sn, cs, ra, rb);
+    Elem<T>::store1(row + ia, ra);
+    Elem<T>::store1(row + ib, rb);
   }
 }
 

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     names = _declared()
     assert {"rgc_rope_apply", "rgc_kv_cache_append", "rgc_rope_append", "rgc_norm_rope_append",
             "rgc_gqa_attn_prefill",
-            "rgc_gqa_attn_decode", "rgc_gqa_attn_decode_workspace_size",
+            "rgc_gqa_attn_decode", "rgc_gqa_attn_decode_workspace_size", "rgc_gqa_attn_decode_rope_append",
             "rgc_diff_attn_prefill", "rgc_gqa_attn_prefill_varlen", "rgc_rope_backward",
             "rgc_gqa_attn_backward", "rgc_gqa_attn_backward_workspace_size"} <= set(names)
     for n in names:
@@ -160,6 +160,42 @@ def test_decode_rejects_bad_arguments_before_launch():
     assert _decode(kv_ss=68) == LAYOUT
     assert _decode(D=48) == HEADDIM
     assert _decode(B=0) == OK
+
+
+ARG = -10
+
+
+def _decode_rope(**kw):
+    a = dict(o=A, q=A, kn=A, vn=A, k=A, v=A, dt=BF16, B=2, Hq=4, Hkv=2, D=64, S_max=32, q_sb=256, q_sh=64,
+             n_sb=128, n_sh=64, o_sb=256, o_sh=64, kv_sb=2 * 32 * 64, kv_sh=32 * 64, kv_ss=64, lens=A,
+             max_len=32, base=10000.0, style=0, scale=0.125, ws=A, ws_bytes=1 << 20, lse=None, err=None)
+    a.update(kw)
+    return rgc.library().rgc_gqa_attn_decode_rope_append(
+        a["o"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["D"],
+        a["S_max"], a["q_sb"], a["q_sh"], a["n_sb"], a["n_sh"], a["o_sb"], a["o_sh"], a["kv_sb"], a["kv_sh"],
+        a["kv_ss"], a["lens"], a["max_len"], a["base"], a["style"], a["scale"], a["ws"], a["ws_bytes"],
+        a["lse"], a["err"], None)
+
+
+def test_fused_decode_step_rejects_bad_arguments_before_launch():
+    assert _decode_rope(dt=F32) == DTYPE  # the fused step is bf16 only
+    assert _decode_rope(dt=7) == DTYPE
+    assert _decode_rope(style=2) == ARG
+    assert _decode_rope(base=0.0) == ARG
+    assert _decode_rope(base=float("inf")) == ARG
+    assert _decode_rope(scale=float("nan")) == ARG
+    assert _decode_rope(Hq=6, Hkv=4) == GROUP
+    assert _decode_rope(D=48) == HEADDIM
+    assert _decode_rope(kn=None) == NULL
+    assert _decode_rope(vn=None) == NULL
+    assert _decode_rope(lens=None) == NULL
+    assert _decode_rope(kn=A + 2) == LAYOUT
+    assert _decode_rope(n_sh=60) == LAYOUT
+    assert _decode_rope(max_len=33) == CAPACITY
+    assert _decode_rope(ws=None) == WORKSPACE
+    assert _decode_rope(ws_bytes=16) == WORKSPACE
+    assert _decode_rope(ws=A + 16) == LAYOUT
+    assert _decode_rope(B=0) == OK
 
 
 def test_decode_workspace_size_grows_with_the_split_count():
