@@ -2,7 +2,8 @@
 
 * tiny (fp32): the whole path, every output element, at 1e-5.
 * llama125m (bf16): two of the twelve independent layers, prefill 512 then
-  100 cached decode steps, every output element.
+  100 cached decode steps, every output element; a third layer with every
+  step as one gqa_attn_decode_rope_append call.
 * prefill3p8b and ragged_decode at full size, in the launch configuration
   the benchmark times: sampled rows checked against the oracle row by row.
 """
@@ -61,6 +62,29 @@ def _gpu_chain(w, q, k, v, S_max):
     return pre, torch.stack(dec, dim=1)
 
 
+def _gpu_chain_one_launch(w, q, k, v, S_max):
+    """GPU: the prompt as above, then each new token's RoPE, append and
+    decode in one gqa_attn_decode_rope_append call (q and k unrotated)."""
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    T = w.S + w.steps
+    pos0 = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    qp, kp = q[:, :w.S].clone(), k[:, :w.S].clone()
+    rgc.rope_apply(qp, pos0)
+    rgc.rope_apply(kp, pos0)
+    kc = torch.zeros((w.B, w.Hkv, S_max, w.D), dtype=w.dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    rgc.kv_cache_append(kc, vc, kp, v[:, :w.S], pos0)
+    pre = rgc.gqa_attn_prefill(qp, kc, vc, pos0)
+    lens = torch.full((w.B,), w.S, dtype=torch.int32, device="cuda")
+    ws = rgc.decode_workspace(w.B, w.Hq, w.Hkv, w.D, T)
+    dec = []
+    for t in range(w.steps):
+        s = w.S + t
+        lens += 1
+        dec.append(rgc.gqa_attn_decode_rope_append(q[:, s], k[:, s], v[:, s], kc, vc, lens, T, ws))
+    return pre, torch.stack(dec, dim=1)
+
+
 def test_tiny_workload_end_to_end_fp32():
     w = synth.WORKLOADS["tiny"]
     T = w.S + w.steps
@@ -81,6 +105,17 @@ def test_llama125m_layer_end_to_end_bf16(layer):
     pre, dec = _gpu_chain(w, q, k, v, T)
     assert_close(pre, ref_pre, torch.bfloat16, "125m prefill")
     assert_close(dec, ref_dec, torch.bfloat16, "125m decode")
+
+
+def test_llama125m_layer_end_to_end_one_launch_steps():
+    w = synth.WORKLOADS["llama125m"]
+    T = w.S + w.steps
+    g = synth.generator(w.seed * 1000 + 5)
+    q, k, v = synth.qkv(w.B, T, w.Hq, w.Hkv, w.D, g, w.dtype)
+    ref_pre, ref_dec = _oracle_chain(w, q, k, v, T)
+    pre, dec = _gpu_chain_one_launch(w, q, k, v, T)
+    assert_close(pre, ref_pre, torch.bfloat16, "125m prefill")
+    assert_close(dec, ref_dec, torch.bfloat16, "125m one-launch decode steps")
 
 
 def test_prefill3p8b_full_size_sampled_rows():
