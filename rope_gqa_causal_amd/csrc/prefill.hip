@@ -17,8 +17,9 @@
 //    probabilities are already in the B-operand layout of O^T = V^T P^T --
 //    P never leaves registers;
 //  * 64-key K and V tiles are staged HBM -> registers -> LDS through a
-//    3-slot ring (tile j read, j+1 ready, j+2 written), one barrier per tile;
-//    the global loads of tile j+2 are in flight while tile j is multiplied;
+//    4-slot ring (tile j read, j+1 ready, j+2 written, j-1 still being read
+//    by slower waves), so one barrier per two tiles suffices; the global
+//    loads of tile j+2 are in flight while tile j is multiplied;
 //  * both tiles stay row-major in LDS with a per-row XOR swizzle of their
 //    16-byte chunks: K fragments (A operand of S^T) are conflict-free 16-byte
 //    reads, and V^T fragments (A operand of O^T) come straight from the
@@ -49,7 +50,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;   // query positions per workgroup
 constexpr int kKT = 64;            // keys per tile
-constexpr int kSlots = 3;          // LDS ring: tile j read, j+1 ready, j+2 written
+constexpr int kSlots = 4;          // LDS ring: tile j read, j+1 ready, j+2 written, j-1 draining
 constexpr int kXcds = 8;           // MI355X: workgroup i is dispatched to XCD i % 8
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kSumTrigger = 256.0f;      // 2^kRescaleThreshold
@@ -244,7 +245,10 @@ __device__ __forceinline__ void compute_tile(WaveCtx<D>& w, int j0) {
 }
 
 // One step of the ring for tile jt in slot SLOT: fetch tile jt+2, multiply
-// tile jt, store tile jt+2 into the slot tile jt-1 used, barrier.
+// tile jt, store tile jt+2 into the slot tile jt-2 used, and on odd steps
+// wait for every wave.  A store into tile jt-2's slot follows the barrier of
+// step jt-1 or jt-2, so every wave has finished that tile; a tile stored in
+// step jt is read in step jt+2, after the barrier of step jt or jt+1.
 template <int D, int SLOT>
 __device__ __forceinline__ void ring_step(WaveCtx<D>& w, u32x4 (&st)[Tile<D>::LOADS], const Stager<D>& sg,
                                           char* lds, const char* kb, const char* vb, int64_t kv_ss, int jt,
@@ -256,7 +260,7 @@ __device__ __forceinline__ void ring_step(WaveCtx<D>& w, u32x4 (&st)[Tile<D>::LO
     else compute_tile<D, SLOT, true>(w, jt * kKT);
   }
   if (refill) store_tile<D, (SLOT + 2) % kSlots>(st, sg, lds);
-  __syncthreads();
+  if (SLOT & 1) __syncthreads();
 }
 
 // D: head dim (32, 64 or 128).
@@ -386,6 +390,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
     ring_step<D, 1>(w, st, sg, lds, kb, vb, p.kv_ss, jt + 1, nkt, kmax, wave_last, diag_from, wave, lane);
     if (jt + 2 >= nkt) break;
     ring_step<D, 2>(w, st, sg, lds, kb, vb, p.kv_ss, jt + 2, nkt, kmax, wave_last, diag_from, wave, lane);
+    if (jt + 3 >= nkt) break;
+    ring_step<D, 3>(w, st, sg, lds, kb, vb, p.kv_ss, jt + 3, nkt, kmax, wave_last, diag_from, wave, lane);
   }
 
   // ---- epilogue: O = O^T / l, rounded to bf16 ----
