@@ -14,7 +14,8 @@
 //    holds one query's column and each map's softmax is in-lane plus one
 //    v_permlane32_swap;
 //  * 64-key tiles of K1, K2 and V are staged HBM -> registers -> LDS through
-//    a 3-slot ring, one barrier per tile;
+//    a 4-slot ring (tile j+2 is stored into tile j-2's slot), one barrier per
+//    two tiles;
 //  * the maps are processed one after the other inside a tile (scores,
 //    softmax, O update), so only one map's scores and probabilities are live
 //    at a time; both read the same staged value tile;
@@ -34,7 +35,7 @@ namespace {
 template <int D>
 constexpr int waves_for() { return 8; }
 constexpr int kKT = 64;            // keys per tile
-constexpr int kSlots = 3;          // LDS ring: tile j read, j+1 ready, j+2 written
+constexpr int kSlots = 4;          // LDS ring: tile j read, j+1 ready, j+2 written, j-1 draining
 constexpr int kXcds = 8;           // MI355X: workgroup i is dispatched to XCD i % 8
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
@@ -238,7 +239,10 @@ __device__ __forceinline__ void ring_step(DiffCtx<D>& w, u32x4 (&st)[DTile<D>::L
     else compute_tile<D, SLOT, true>(w, jt * kKT);
   }
   if (refill) store_tile<D, (SLOT + 2) % kSlots>(st, sg, lds);
-  __syncthreads();
+  // A store into tile jt-2's slot follows the barrier of step jt-1 or jt-2;
+  // a tile stored in step jt is read in step jt+2, after the barrier of step
+  // jt or jt+1: odd steps alone wait for every wave.
+  if (SLOT & 1) __syncthreads();
 }
 
 template <int D>
@@ -348,6 +352,8 @@ __global__ void __launch_bounds__(64 * waves_for<D>(), 1) diff_kernel(DiffParams
     ring_step<D, 1>(w, st, sg, lds, base, p.kv_ss, jt + 1, nkt, kmax, wave_last, diag_from, wave, lane);
     if (jt + 2 >= nkt) break;
     ring_step<D, 2>(w, st, sg, lds, base, p.kv_ss, jt + 2, nkt, kmax, wave_last, diag_from, wave, lane);
+    if (jt + 3 >= nkt) break;
+    ring_step<D, 3>(w, st, sg, lds, base, p.kv_ss, jt + 3, nkt, kmax, wave_last, diag_from, wave, lane);
   }
 
   // ---- epilogue: o = O1 / l1 - lambda * O2 / l2, rounded once to bf16 ----
