@@ -27,6 +27,11 @@ BACKWARD_CASES = [
     (2, 77, 8, 1, 32),      # MQA, D 32
     (1, 161, 24, 8, 128),   # the 3.8B head layout
     (1, 1, 2, 1, 64),       # a single row
+    # dQ's pipelined loop: several unmasked steps with a previous tile, the
+    # diagonal tile and the tail, and a ragged last key tile (1000 = 15 x 64 + 40)
+    (1, 1000, 4, 2, 128),
+    (1, 640, 2, 1, 64),     # whole 64-key tiles only (no ragged tile), D 64
+    (1, 129, 2, 2, 32),     # one row past a 128-row block, D 32
 ]
 
 
