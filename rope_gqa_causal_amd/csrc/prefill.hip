@@ -273,23 +273,29 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
   // XCD-aware order.  Workgroup i runs on XCD i % 8.  Units u = (sequence,
   // KV head) stay on one XCD, so the query heads of a unit share its K/V in
   // that XCD's L2 (and the MALL behind it).  XCD x takes the units u = x
-  // (mod 8) and walks them q-tile slab by q-tile slab, heaviest slab first
-  // across all its units, so the heavy tiles start at once and the light
-  // ones fill the end: walking unit by unit instead (heaviest tile first
-  // within each unit) leaves heavy tiles of the last units for the end, and
-  // the last compute unit finishes 11 % after the average (108 against 120
-  // tile-steps per compute unit on the 3.8B-shaped batch).
+  // (mod 8) in groups of four and walks each group q-tile slab by slab,
+  // heaviest slab first, so heavy tiles start early and light ones fill the
+  // end.  Walking unit by unit (heaviest tile first within each unit) leaves
+  // heavy tiles of the last units for the end: on the 3.8B-shaped batch the
+  // busiest compute unit then carries 120 tile-steps against an average of
+  // 108 (112 with groups of four).  Larger groups balance a little better
+  // but spread a unit's q-tiles over more time, so its K/V tiles are
+  // fetched again; packed documents, whose lengths differ widely, use one
+  // group (all their units) so the long documents' heavy tiles start at once.
   const int group = p.Hq / p.Hkv;
   int qt, b, kvh, h;
   {
     const int units = p.B * p.Hkv;
     const int x = (int)(blockIdx.x % kXcds), r = (int)(blockIdx.x / kXcds);
     const int cnt = x < units ? (units - x + kXcds - 1) / kXcds : 0;  // units u = x (mod 8)
-    const int per_slab = cnt * group;
-    if (r >= per_slab * nqt) return;
-    const int within = r % per_slab;
-    qt = nqt - 1 - r / per_slab;
-    const int u = x + kXcds * (within / group);
+    if (r >= cnt * group * nqt) return;
+    const int G = p.cu_seqlens ? cnt : 4;  // units walked together, slab by slab
+    const int gi = r / (G * group * nqt), g0 = gi * G, gn = min(G, cnt - g0);
+    const int rr = r - gi * G * group * nqt;
+    const int per_slab = gn * group;
+    const int within = rr % per_slab;
+    qt = nqt - 1 - rr / per_slab;
+    const int u = x + kXcds * (g0 + within / group);
     kvh = u % p.Hkv;
     b = u / p.Hkv;
     h = kvh * group + within % group;
