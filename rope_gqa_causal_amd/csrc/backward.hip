@@ -10,8 +10,7 @@
 // where Dlt_i = sum_j w_ij dP_ij = dO_i . o_i, and dK, dV sum over the query
 // heads of each KV head's group.
 //
-// Three kernels, no atomics:
-//  * delta_kernel: Dlt_i = dO_i . o_i (fp32) per (sequence, head, row);
+// Two kernels, no atomics:
 //  * dkdv_kernel: a workgroup owns 128 keys of one (sequence, KV head) (32
 //    per wave, K and V in LDS) and walks every query head of the group and
 //    every query block of 64 rows at or after its keys (the next block's
@@ -21,8 +20,10 @@
 //    key and P, dS are already the A operand of dV += P^T dO and
 //    dK += dS^T Q; dO and Q enter those as transposed fragments
 //    (ds_read_b64_tr_b16) of the row-major tiles;
-//  * dq_kernel (backward_dq.hip): a workgroup owns 128 query rows of one
-//    (sequence, head) and walks the 64-key tiles at or before them.
+//  * dq_kernel (backward_dq.hip), launched first: a workgroup owns 128
+//    query rows of one (sequence, head), forms their Dlt_i = dO_i . o_i
+//    (fp32) into the workspace, and walks the 64-key tiles at or before
+//    them.
 // The weights are recomputed from the forward pass's lse; P and dS are
 // rounded to bf16 for the MFMAs, everything accumulates in fp32, and dq, dk,
 // dv are rounded once to bf16.
@@ -47,34 +48,6 @@ __device__ __forceinline__ void stage_rows(char* tile, const bf16_t* g, int64_t 
   }
 }
 
-// ---------------------------------------------------------------------------
-// Dlt = rowsum(dO * O) in fp32: one row per 16 lanes (8 elements per lane at
-// D = 128; 4 or 2 lanes' worth at smaller D fold the same way).
-__global__ void __launch_bounds__(256) delta_kernel(BwdParams p, float* dlt) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b, h, i) with i fastest
-  const int sub = threadIdx.x & 15;
-  const int64_t nrows = (int64_t)p.B * p.Hq * p.S;
-  float acc = 0.f;
-  int64_t b = 0, h = 0, i = 0;
-  if (row < nrows) {
-    i = row % p.S;
-    h = (row / p.S) % p.Hq;
-    b = row / ((int64_t)p.S * p.Hq);
-    const int64_t off = b * p.q_sb + i * p.q_ss + h * p.q_sh;
-    for (int c = sub; c < p.D / 8; c += 16) {
-      const u32x4 a = ld16(reinterpret_cast<const bf16_t*>(p.dO) + off + 8 * c);
-      const u32x4 o = ld16(reinterpret_cast<const bf16_t*>(p.o) + off + 8 * c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(bf16_lo(a[e]), bf16_lo(o[e]), acc);
-        acc = fmaf(bf16_hi(a[e]), bf16_hi(o[e]), acc);
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < nrows && sub == 0) dlt[row] = acc;
-}
 
 constexpr int kKeysPerWave = 32;
 constexpr int kDkdvWaves = 4;
@@ -336,12 +309,13 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) dkdv_kernel(BwdParams p, cons
 
 template <int D>
 hipError_t launch_d(const BwdParams& p, float* dlt, hipStream_t stream) {
+  // dQ first: it forms Dlt, which dK/dV reads.
+  hipError_t e = launch_dq_bf16(p, dlt, stream);
+  if (e != hipSuccess) return e;
   const int nkb = (p.S + kKeyBlock - 1) / kKeyBlock;
   hipLaunchKernelGGL(dkdv_kernel<D>, dim3((unsigned)(p.B * p.Hkv * nkb)), dim3(kDkdvThreads),
                      (size_t)DkdvLds<D>::BYTES, stream, p, (const float*)dlt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_dq_bf16(p, dlt, stream);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -352,10 +326,6 @@ size_t backward_workspace_bytes(int B, int S, int Hq) {
 
 hipError_t launch_backward_bf16(const BwdParams& p, void* workspace, hipStream_t stream) {
   float* dlt = reinterpret_cast<float*>(workspace);
-  const int64_t rows = (int64_t)p.B * p.Hq * p.S;
-  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, dlt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   switch (p.D) {
     case 32: return launch_d<32>(p, dlt, stream);
     case 64: return launch_d<64>(p, dlt, stream);

@@ -1,6 +1,6 @@
 // backward_dq.hip -- dQ of causal GQA self-attention (bf16, MFMA), the
-// third kernel of the training pass whose other two kernels (Dlt and dK/dV)
-// are in backward.hip.
+// first of the training pass's two kernels (dK/dV is in backward.hip); it
+// also forms Dlt_i = dO_i . o_i, which the dK/dV kernel reads.
 //
 // For row i of query head h, with weights w_ij = softmax_j(scale q_i.k_j)
 // over keys j <= i, dP_ij = dO_i . v_j and Dlt_i = dO_i . o_i:
@@ -224,7 +224,7 @@ __device__ __forceinline__ void dq_tail(const char* prev, const DqOffsets<D>& of
 }
 
 template <int D>
-__global__ void __launch_bounds__(kDqThreads, 1) dq_kernel(BwdParams p, const float* dlt) {
+__global__ void __launch_bounds__(kDqThreads, 1) dq_kernel(BwdParams p, float* dlt) {
   using T = BTile<D>;
   using L = DqLds<D>;
   constexpr int KS = T::KS, DB = T::DB;
@@ -251,7 +251,22 @@ __global__ void __launch_bounds__(kDqThreads, 1) dq_kernel(BwdParams p, const fl
     dof[ks] = qvalid ? ld16(reinterpret_cast<const bf16_t*>(p.dO) + qoff + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
   }
   const float lse2 = qvalid ? p.lse[((int64_t)b * p.Hq + h) * p.S + qi] * kAttnLog2e : 0.f;
-  const float dl = qvalid ? dlt[((int64_t)b * p.Hq + h) * p.S + qi] : 0.f;
+  // Dlt_i = dO_i . o_i in fp32: lanes l and l ^ 32 each hold half of the
+  // query's dO and o rows.  This kernel runs before the dK/dV kernel and
+  // leaves Dlt in the workspace for it.
+  float dl = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 ov =
+        qvalid ? ld16(reinterpret_cast<const bf16_t*>(p.o) + qoff + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dl = fmaf(bf16_lo(dof[ks][e]), bf16_lo(ov[e]), dl);
+      dl = fmaf(bf16_hi(dof[ks][e]), bf16_hi(ov[e]), dl);
+    }
+  }
+  dl += __shfl_xor(dl, 32, 64);
+  if (qvalid && half == 0) dlt[((int64_t)b * p.Hq + h) * p.S + qi] = dl;
 
   f32x16 acc[DB], sm[2], dp[2];
 #pragma unroll
@@ -383,7 +398,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) dq_kernel(BwdParams p, const fl
 
 }  // namespace
 
-hipError_t launch_dq_bf16(const BwdParams& p, const float* dlt, hipStream_t stream) {
+hipError_t launch_dq_bf16(const BwdParams& p, float* dlt, hipStream_t stream) {
   const int nqt = (p.S + kDqRows - 1) / kDqRows;
   const dim3 grid((unsigned)(p.B * p.Hq * nqt)), block(kDqThreads);
   switch (p.D) {

@@ -107,8 +107,8 @@ struct BwdParams {
 };
 size_t backward_workspace_bytes(int B, int S, int Hq);
 hipError_t launch_backward_bf16(const BwdParams& p, void* workspace, hipStream_t stream);
-// The dQ kernel alone, after Dlt (dlt, [B,Hq,S] fp32) is in place.
-hipError_t launch_dq_bf16(const BwdParams& p, const float* dlt, hipStream_t stream);
+// The dQ kernel; it also writes Dlt = rowsum(dO * O) ([B,Hq,S] fp32) to dlt.
+hipError_t launch_dq_bf16(const BwdParams& p, float* dlt, hipStream_t stream);
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len);
 hipError_t launch_decode_bf16(const AttnParams& p, void* ws, hipStream_t stream);
