@@ -12,7 +12,10 @@ One step = one pass of the whole path over one batch of synthetic input:
 must read / decode-phase time, GB/s); the prefill phase's attention rate is
 reported beside it (TFLOP/s over unmasked query-key pairs).  Both are also
 given per kernel against the MI355X peaks (HBM 8 TB/s; dense bf16 MFMA
-2.5 PFLOP/s), from HIP events recorded on the stream the kernels run on.
+2.5 PFLOP/s), from HIP events recorded on the stream the kernels run on: the
+decode's dominant kernel (the split-K kernel that streams the cache) is timed
+by the library's per-kernel events, and the whole decode op (split + merge)
+is reported beside it.
 The differential-attention variant (`diff_attn`), the packed-document prefill
 (`varlen_prefill`), the fused prologue with and without QK normalisation
 (`prologue`), the attention backward (`backward`) and the 125M-shaped cached
@@ -126,8 +129,11 @@ def summarize_pmc(fetch_dir, write_dir):
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(kind, json.dumps(rec))
-    record("decode", "decode.hip", ["decode_split_kernel", "decode_combine_kernel"],
-           "average over the 32 decode calls of one bench step (cache lengths grow by one per call)")
+    record("decode", "decode.hip", ["decode_split_kernel"],
+           "the decode's dominant kernel, average over the 32 decode calls of one bench step "
+           "(cache lengths grow by one per call)")
+    record("decode_op", "decode.hip", ["decode_split_kernel", "decode_combine_kernel"],
+           "the whole decode op (split + merge), average over the 32 decode calls of one bench step")
     record("prefill", "prefill.hip", ["prefill_kernel"], "one prefill launch of the bench step")
 
 
@@ -185,29 +191,21 @@ class Decode:
         # sequence, new token included (lengths lens0 + t + 1).
         per_token = w.Hkv * w.D * 2 * 2
         self.bytes_per_call = [per_token * float((self.lens0_cpu + t + 1).sum()) for t in range(w.steps)]
-        self.events = []
 
-    def run(self, record, fused=False):
+    def run(self, fused=False):
         r, w = self.rgc, self.w
         for t in range(w.steps):
             if not fused:
                 # the two-launch form: RoPE (q, k at position lens0 + t) and
                 # cache append, then the decode of the rotated q
                 r.rope_append(self.q[t], self.k[t], self.v[t], self.kc, self.vc, self.slots[t])
-            if record:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-            if fused:
+                r.gqa_attn_decode(self.q[t][:, 0], self.kc, self.vc, self.lens[t], self.S_max, self.ws,
+                                  out=self.o)
+            else:
                 # one launch (plus the chunk merge): RoPE of q and k at
                 # position lens0 + t, append of k and v, attention
                 r.gqa_attn_decode_rope_append(self.q[t][:, 0], self.k[t][:, 0], self.v[t][:, 0], self.kc,
                                               self.vc, self.lens[t], self.S_max, self.ws, out=self.o)
-            else:
-                r.gqa_attn_decode(self.q[t][:, 0], self.kc, self.vc, self.lens[t], self.S_max, self.ws,
-                                  out=self.o)
-            if record:
-                e1.record()
-                self.events.append((t, e0, e1))
 
 
 class Diff:
@@ -498,7 +496,7 @@ def main():
 
     for i in range(args.warmup):
         pre.run(False)
-        dec.run(False)
+        dec.run()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
@@ -507,6 +505,7 @@ def main():
     phase = []
     torch.cuda.synchronize()
     t_start.record()
+    rgc.timing_report()  # clear
     for i in range(args.steps):
         a = torch.cuda.Event(enable_timing=True)
         m = torch.cuda.Event(enable_timing=True)
@@ -514,14 +513,21 @@ def main():
         a.record()
         pre.run(True)
         m.record()
-        # Per-call events break the back-to-back issue of the decode calls
-        # (about 7 us per call here), so only the last timed step carries
-        # them; the decode roofline averages that step's 32 launches.
-        dec.run(i == args.steps - 1)
+        # Events between the decode kernels break their back-to-back issue
+        # (a few us per call), so only the last timed step carries them: the
+        # library brackets each kernel it launches there, and the decode
+        # roofline averages that step's 32 launches.
+        last = i == args.steps - 1
+        if last:
+            rgc.timing_enable(True)
+        dec.run()
+        if last:
+            rgc.timing_enable(False)
         z.record()
         phase.append((a, m, z))
     t_end.record()
     torch.cuda.synchronize()
+    ktimes = rgc.timing_report()
     print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
 
     total_ms = t_start.elapsed_time(t_end)
@@ -531,13 +537,20 @@ def main():
     value = dec_bytes / (dec_ms * 1e-3) / 1e9
     prefill_tflops = pre.flops * args.steps / (pre_ms * 1e-3) / 1e12
 
-    # Per-launch kernel durations (HIP events around each call).
+    # Per-launch kernel durations: the prefill from HIP events around each
+    # call (one kernel per call), the decode kernels from the library's own
+    # per-kernel events in the last timed step.
     pk_ms = [e0.elapsed_time(e1) for e0, e1 in pre.events]
-    dk = [(t, e0.elapsed_time(e1)) for t, e0, e1 in dec.events]
     pk_avg = sum(pk_ms) / len(pk_ms)
-    dk_avg = sum(ms for _, ms in dk) / len(dk)
-    dk_bytes_avg = sum(dec.bytes_per_call[t] for t, _ in dk) / len(dk)
+    n_split, split_us = ktimes["decode_split_kernel"]
+    n_comb, comb_us = ktimes.get("decode_combine_kernel", (n_split, 0.0))
+    if n_split != dec.w.steps or n_comb != dec.w.steps:
+        raise SystemExit(f"expected {dec.w.steps} decode launches per kernel, got {ktimes}")
+    dk_avg = split_us / n_split * 1e-3               # ms
+    op_avg = dk_avg + comb_us / n_comb * 1e-3        # ms, kernel time of split + merge
+    dk_bytes_avg = sum(dec.bytes_per_call) / len(dec.bytes_per_call)
     dec_achieved = dk_bytes_avg / (dk_avg * 1e-3) / 1e9
+    op_achieved = dk_bytes_avg / (op_avg * 1e-3) / 1e9
     pre_achieved = pre.flops / (pk_avg * 1e-3) / 1e12
 
     result = {
@@ -568,7 +581,7 @@ def main():
         "decode_phase_ms_per_step": round(dec_ms / args.steps, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "gqa_attn_decode (split-K + combine)",
+            "kernel": "decode_split_kernel (the decode's dominant kernel: streams the cache)",
             "achieved": round(dec_achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -576,6 +589,13 @@ def main():
             "traffic": stored_traffic("decode", "decode.hip", dk_bytes_avg),
             "algorithmic_bytes_per_launch": round(dk_bytes_avg),
             "avg_launch_us": round(dk_avg * 1e3, 3),
+            "op": {
+                "kernels": "decode_split_kernel + decode_combine_kernel (gqa_attn_decode)",
+                "avg_kernel_us": round(op_avg * 1e3, 3),
+                "achieved": round(op_achieved, 2),
+                "frac": round(op_achieved / HBM_PEAK_GBS, 4),
+                "traffic": stored_traffic("decode_op", "decode.hip", dk_bytes_avg),
+            },
         },
         "roofline_prefill": {
             "bound": "mfma",

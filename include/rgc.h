@@ -85,6 +85,25 @@ int rgc_abi_version(void);
 const char* rgc_status_string(int status);
 
 /*
+ * Per-kernel timing, for measurement.  While on, every kernel the library
+ * launches is bracketed by two HIP events recorded on the stream it runs
+ * on, so each kernel's own duration is taken on the device clock apart from
+ * the other kernels of the same call (each event pair costs a few
+ * microseconds of stream time, so leave it off outside measurement).
+ *   rgc_timing_enable   on != 0 starts recording, 0 stops (what was
+ *                       recorded stays until the next report).  RGC_OK.
+ *   rgc_timing_report   waits for the recorded events, writes one line
+ *                       "kernel_name launches total_microseconds\n" per
+ *                       kernel into buf (NUL-terminated) and clears the
+ *                       record.  Returns the bytes written without the NUL,
+ *                       or RGC_ERR_ARG when buf is NULL or too small or an
+ *                       event could not be read (the record is cleared in
+ *                       every case).  Host-thread safe.
+ */
+int rgc_timing_enable(int on);
+long rgc_timing_report(char* buf, size_t buf_bytes);
+
+/*
  * rgc_rope_apply -- rotary position embedding, in place.
  *   x     [B,S,H,D] of dtype, strides (sb, ss, sh); rotated in place.
  *   pos0  [B] int32 or NULL (all zero): token (b, s) sits at position

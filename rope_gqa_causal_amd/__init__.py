@@ -25,7 +25,7 @@ __all__ = [
     "gqa_attn_prefill",
     "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace", "diff_attn_prefill",
     "gqa_attn_prefill_varlen", "rope_backward", "gqa_attn_backward", "backward_workspace",
-    "ROPE_HALF", "ROPE_INTERLEAVED",
+    "ROPE_HALF", "ROPE_INTERLEAVED", "timing_enable", "timing_report",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,6 +43,8 @@ _sz = ctypes.c_size_t
 _SIGNATURES = {
     "rgc_abi_version": (_i, []),
     "rgc_status_string": (ctypes.c_char_p, [_i]),
+    "rgc_timing_enable": (_i, [_i]),
+    "rgc_timing_report": (ctypes.c_long, [ctypes.c_char_p, _sz]),
     "rgc_rope_apply": (_i, [_p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _d, _i, _p]),
     "rgc_rope_backward": (_i, [_p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _d, _i, _p]),
     "rgc_gqa_attn_backward_workspace_size": (_sz, [_i, _i, _i]),
@@ -134,6 +136,26 @@ def _lens(t, B, name):
     if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
         raise ValueError(f"{name} must be a contiguous int32 tensor of {B} elements")
     return t
+
+
+def timing_enable(on=True):
+    """Start (or stop) per-kernel timing: each kernel the library launches is
+    bracketed by HIP events on its own stream until switched off."""
+    _call("rgc_timing_enable", 1 if on else 0)
+
+
+def timing_report():
+    """Per-kernel {name: (launches, total microseconds)} recorded since the
+    last report (waits for the events; clears the record)."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = library().rgc_timing_report(buf, len(buf))
+    if n < 0:
+        raise RgcError("rgc_timing_report", n, library().rgc_status_string(n).decode())
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, calls, us = line.split()
+        out[name] = (int(calls), float(us))
+    return out
 
 
 def rope_apply(x, pos0=None, base=10000.0, style=ROPE_HALF):

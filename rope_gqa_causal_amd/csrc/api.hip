@@ -528,4 +528,11 @@ int rgc_gqa_attn_decode_rope_append(void* o, const void* q, const void* k_new, c
   return hip_status(launch_decode_rope_bf16(p, r, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int rgc_timing_enable(int on) { return timing_enable(on); }
+
+long rgc_timing_report(char* buf, size_t buf_bytes) {
+  const long n = timing_report(buf, buf_bytes);
+  return n < 0 ? (long)RGC_ERR_ARG : n;
+}
+
 }  // extern "C"

@@ -45,6 +45,7 @@ hipError_t launch_append(const AppendParams& p, int dtype, hipStream_t stream) {
   const int64_t n = (int64_t)p.B * p.S_new * p.Hkv * (p.D * esz / 16);
   const int block = 256;
   const dim3 grid((unsigned)((n + block - 1) / block));
+  KernelTimer kt_("append_kernel", stream);
   if (esz == 4)
     hipLaunchKernelGGL(append_kernel<4>, grid, dim3(block), 0, stream, p);
   else

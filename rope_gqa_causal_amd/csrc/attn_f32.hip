@@ -105,6 +105,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnParams p, int decode) 
 hipError_t launch_attn_f32(const AttnParams& p, bool decode, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.B * p.Sq * p.Hq));
   const int dec = decode ? 1 : 0;
+  KernelTimer kt_("attn_f32_kernel", stream);
   switch (p.D) {
     case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(64), 0, stream, p, dec); break;
     case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, p, dec); break;

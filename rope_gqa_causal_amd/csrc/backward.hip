@@ -313,6 +313,7 @@ hipError_t launch_d(const BwdParams& p, float* dlt, hipStream_t stream) {
   hipError_t e = launch_dq_bf16(p, dlt, stream);
   if (e != hipSuccess) return e;
   const int nkb = (p.S + kKeyBlock - 1) / kKeyBlock;
+  KernelTimer kt_("dkdv_kernel", stream);
   hipLaunchKernelGGL(dkdv_kernel<D>, dim3((unsigned)(p.B * p.Hkv * nkb)), dim3(kDkdvThreads),
                      (size_t)DkdvLds<D>::BYTES, stream, p, (const float*)dlt);
   return hipGetLastError();

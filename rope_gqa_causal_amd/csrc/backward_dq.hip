@@ -401,6 +401,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) dq_kernel(BwdParams p, float* d
 hipError_t launch_dq_bf16(const BwdParams& p, float* dlt, hipStream_t stream) {
   const int nqt = (p.S + kDqRows - 1) / kDqRows;
   const dim3 grid((unsigned)(p.B * p.Hq * nqt)), block(kDqThreads);
+  KernelTimer kt_("dq_kernel", stream);
   switch (p.D) {
     case 32: hipLaunchKernelGGL(dq_kernel<32>, grid, block, (size_t)DqLds<32>::BYTES, stream, p, dlt); break;
     case 64: hipLaunchKernelGGL(dq_kernel<64>, grid, block, (size_t)DqLds<64>::BYTES, stream, p, dlt); break;

@@ -460,6 +460,7 @@ int heads_per_wg(int group) {
 template <int D, int MUL, bool ROPE>
 hipError_t launch_dm(const AttnParams& p, const DecodeRope& r, DecodeWs ws, int gs, int nsub, hipStream_t stream) {
   const dim3 grid(ws.NS, p.Hkv * nsub, p.B), block(64 * kWaves);
+  KernelTimer kt_("decode_split_kernel", stream);
   switch (gs) {
     case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, MUL, ROPE>), grid, block, 0, stream, p, ws, nsub, r); break;
     case 3: hipLaunchKernelGGL((decode_split_kernel<D, 3, MUL, ROPE>), grid, block, 0, stream, p, ws, nsub, r); break;
@@ -490,6 +491,7 @@ hipError_t launch_d(const AttnParams& p, const DecodeRope& r, DecodeWs ws, hipSt
   hipError_t e = mul == 2 ? launch_dm<D, 2, ROPE>(p, r, ws, gs, nsub, stream)
                           : launch_dm<D, 1, ROPE>(p, r, ws, gs, nsub, stream);
   if (e != hipSuccess || ws.NS <= 1) return e;
+  KernelTimer kt_("decode_combine_kernel", stream);
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((p.B * p.Hq + 3) / 4), dim3(256), 0, stream, p, ws);
   return hipGetLastError();
 }

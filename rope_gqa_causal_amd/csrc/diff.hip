@@ -389,6 +389,7 @@ hipError_t launch_d(const DiffParams& dp, hipStream_t stream) {
   const int nqt = (p.Sq + kBM - 1) / kBM;
   const int total = p.B * p.Hq * nqt;
   const dim3 grid((unsigned)(((total + kXcds - 1) / kXcds) * kXcds));
+  KernelTimer kt_("diff_kernel", stream);
   hipLaunchKernelGGL(diff_kernel<D>, grid, dim3(64 * waves_for<D>()), (size_t)DTile<D>::LDS_BYTES, stream, dp,
                      nqt);
   return hipGetLastError();

@@ -9,6 +9,24 @@
 
 namespace rgc {
 
+// Brackets one kernel launch with HIP events on its stream while per-kernel
+// timing is on (timing.hip); does nothing otherwise.  Construct it right
+// before the launch, in the scope that ends right after it.
+class KernelTimer {
+ public:
+  KernelTimer(const char* name, hipStream_t stream);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+int timing_enable(int on);
+long timing_report(char* buf, size_t bytes);
+
 enum { DT_F32 = 0, DT_BF16 = 1 };
 enum { ROPE_HALF = 0, ROPE_INTERLEAVED = 1 };
 

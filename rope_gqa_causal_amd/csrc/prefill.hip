@@ -429,6 +429,7 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   // every XCD sized for the largest unit share
   const int64_t total = (int64_t)kXcds * ((p.B * p.Hkv + kXcds - 1) / kXcds) * (p.Hq / p.Hkv) * nqt;
   const dim3 grid((unsigned)(((total + kXcds - 1) / kXcds) * kXcds));
+  KernelTimer kt_("prefill_kernel", stream);
   hipLaunchKernelGGL(prefill_kernel<D>, grid, dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream, p, nqt);
   return hipGetLastError();
 }

@@ -260,6 +260,7 @@ hipError_t launch_typed(const RopeParams& p, hipStream_t stream) {
   const bool vec = (p.D % (2 * E) == 0) && (addr % 16 == 0) && (p.sb % E == 0) &&
                    (p.ss % E == 0) && (p.sh % E == 0);
   const int block = 256;
+  KernelTimer kt_(vec ? "rope_vec_kernel" : "rope_scalar_kernel", stream);
   if (vec) {
     const int tpb = tokens_per_block(p.H * (p.D / (2 * E)), p.D);
     hipLaunchKernelGGL((rope_vec_kernel<T, STYLE>), dim3((unsigned)((ntok + tpb - 1) / tpb)), dim3(kBlock), 0,
@@ -278,6 +279,7 @@ hipError_t launch_append_typed(const RopeAppendParams& p, bool norm, hipStream_t
   const int64_t ntok = (int64_t)p.B * p.S;
   const int tpb = tokens_per_block((p.Hq + 2 * p.Hkv) * (p.D / (2 * E)), p.D);
   const dim3 grid((unsigned)((ntok + tpb - 1) / tpb));
+  KernelTimer kt_("rope_append_kernel", stream);
   if (norm)
     hipLaunchKernelGGL((rope_append_kernel<T, STYLE, true>), grid, dim3(kBlock), 0, stream, p, tpb);
   else

@@ -231,3 +231,14 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         rgc.rope_apply(x)
+
+
+def test_timing_switch_and_empty_report():
+    lib = rgc.library()
+    assert lib.rgc_timing_enable(1) == OK
+    assert lib.rgc_timing_enable(0) == OK
+    assert rgc.timing_report() == {}  # nothing launched: no lines
+    buf = ctypes.create_string_buffer(16)
+    assert lib.rgc_timing_report(buf, len(buf)) == 0 and buf.value == b""
+    assert lib.rgc_timing_report(None, 16) == -10  # RGC_ERR_ARG
+    assert lib.rgc_timing_report(buf, 0) == -10
