@@ -412,7 +412,7 @@ def time_backward(rgc, synth, iters):
     us = e0.elapsed_time(e1) / iters * 1e3
     flops = 10.0 * w.D * w.B * w.Hq * w.S * (w.S + 1) / 2  # five products per unmasked pair x 2D
     tf = flops / (us * 1e-6) / 1e12
-    return {"bound": "mfma", "kernel": "gqa_attn_backward (delta + dK/dV + dQ)", "achieved": round(tf, 2),
+    return {"bound": "mfma", "kernel": "gqa_attn_backward (dQ with Dlt, then dK/dV)", "achieved": round(tf, 2),
             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
             "algorithmic_flops_per_launch": flops, "avg_launch_us": round(us, 3),
             "workload": "B8 x 2048, 24q/8kv, D128, bf16; FLOPs count S, dP, dV, dK, dQ (2D each) per unmasked pair"}
