@@ -331,7 +331,11 @@ size_t rgc_gqa_attn_decode_workspace_size(int B, int Hq, int Hkv, int D,
  *             fp32 dtype the workspace is not used (may be NULL).
  *   lse       [B,Hq] fp32 or NULL.
  * Same arithmetic as prefill.  The cache is split along its length; the
- * partial results are merged by max-rescaled sums.  A sequence with
+ * partial results are merged by max-rescaled sums.  When the split would not
+ * give every compute unit a workgroup and max_len is short enough (at most
+ * 2 x 12 x 128, 64 or 32 keys at D = 32, 64, 128), one workgroup per
+ * (sequence, query head) walks the whole cache instead, in one launch.  A
+ * sequence with
  * seq_lens outside [1, min(max_len, S_max)] gets NaN rows and a flag.
  */
 int rgc_gqa_attn_decode(void* o, const void* q, const void* k_cache,

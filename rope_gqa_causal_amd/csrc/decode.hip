@@ -29,7 +29,11 @@
 //    the four waves;
 //  * a chunk's partial (max, sum, unnormalised output) goes to the
 //    workspace and a second, small kernel merges the chunks by max-rescaled
-//    sums.  A sequence that fits in one chunk is finished by the first.
+//    sums.  A sequence that fits in one chunk is finished by the first;
+//  * a grid too small to fill the chip this way (a few sequences, as in
+//    batch-1 generation) takes a third kernel instead: one 12-wave
+//    workgroup per (sequence, query head) walks the whole sequence in at
+//    most two passes and writes the final row, so the step is one launch.
 //    (Merging inside the first kernel, by the last chunk to arrive, would
 //    need device-scope fences, and on gfx950 each of those writes back and
 //    invalidates the XCD's L2: measured 16x slower than the second launch.)
@@ -391,6 +395,279 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
   }
 }
 
+// Small grids: one workgroup of W waves per (sequence, KV head, head
+// subgroup) covers W x WK keys per pass and walks the whole sequence.  q is
+// loaded (with ROPE: loaded and turned) once; every wave carries its running
+// max, sum and output across passes, rescaled when the max rises.  The W
+// waves then merge in LDS and write the final row: no partials and no merge
+// launch.  Used where the split kernel's chunks could not fill the chip
+// anyway (a few sequences, as in batch-1 generation), so its second launch
+// would dominate the step; with 16 waves a sequence of up to 512 or 1024
+// keys takes a single pass.
+template <int D, int GS, int MUL, bool ROPE, int W>
+__global__ void __launch_bounds__(64 * W) decode_loop_kernel(AttnParams p, int nsub, DecodeRope r) {
+  constexpr int WK = Chunk<D, MUL>::WAVE_KEYS;
+  constexpr int KEYS = W * WK;
+  constexpr int LPK = D / 32;      // lanes per key in the q.k layout
+  constexpr int KPP = 64 / LPK;    // keys per pass
+  constexpr int PASSES = WK / KPP; // passes over the wave's keys
+  constexpr int LPR = D / 8;       // lanes per row in the p.V layout
+  constexpr int KPI = 64 / LPR;    // keys per load in the p.V layout
+  constexpr int VLOADS = WK / KPI;
+  constexpr int HALF = D / 2;
+
+  __shared__ f32x4 p_lds[W][WK];
+  __shared__ float o_lds[W][GS][D];
+  __shared__ float ml_lds[W][GS][2];
+  // With ROPE: each wave's turned q rows and the new token's turned k row.
+  __shared__ __attribute__((aligned(16))) bf16_t rows[ROPE ? W : 1][GS + 1][D];
+
+  const int hs = blockIdx.y % nsub;
+  const int kvh = blockIdx.y / nsub;
+  const int b = blockIdx.z;
+  const int group = p.Hq / p.Hkv;
+  const int h0 = kvh * group + hs * GS;
+  const int L = p.seq_lens[b];
+  const int tid = threadIdx.x;
+  if (!len_ok(p, L)) {
+    for (int i = tid; i < GS * D; i += 64 * W) {
+      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)(h0 + i / D) * p.o_sh;
+      orow[i % D] = 0x7FC0;  // NaN
+    }
+    if (tid < GS && p.lse) p.lse[(int64_t)b * p.Hq + h0 + tid] = __builtin_nanf("");
+    if (tid == 0 && p.err) p.err[0] = 1;
+    return;
+  }
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const float c = p.scale * kLog2e;
+  const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
+  const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh;
+  const int part = lane % LPK, key_sub = lane / LPK;
+  const int dgrp = lane % LPR, kq = lane / LPR;
+
+  float m_w[GS], l_w[GS], acc[GS][8];
+#pragma unroll
+  for (int g = 0; g < GS; ++g) {
+    m_w[g] = -INFINITY;
+    l_w[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  }
+
+  // Every load is unconditional: keys past the end re-read the last row and
+  // are masked in the scores.
+  auto load = [&](u32x4 (&kf)[PASSES][4], u32x4 (&vf)[VLOADS], int kw) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int key = min(kw + ps * KPP + key_sub, L - 1);
+      const bf16_t* kr = kbase + (int64_t)key * p.kv_ss;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[ps][i] = ld16(kr + 8 * (part + LPK * i));
+    }
+#pragma unroll
+    for (int t = 0; t < VLOADS; ++t) {
+      const int key = min(kw + t * KPI + kq, L - 1);
+      vf[t] = ld16(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
+    }
+  };
+  // The first pass's K and V loads go out before q's, so the q prologue
+  // (with ROPE: the angle, the rotation and the LDS round trip) runs while
+  // they are in flight.
+  u32x4 kf[PASSES][4], vf[VLOADS];
+  load(kf, vf, wave * WK);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- q in the q.k layout; with ROPE, q and the new token's k turned at
+  // position L - 1 through this wave's LDS rows (the RoPE kernels' angle,
+  // rotation and rounding), and the new token's v ----
+  u32x4 qf[GS][4];
+  u32x4 vn = {};
+  if constexpr (ROPE) {
+    const int ia = r.style == ROPE_HALF ? lane : 2 * lane, ib = r.style == ROPE_HALF ? lane + HALF : 2 * lane + 1;
+    vn = ld16(reinterpret_cast<const bf16_t*>(r.v_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh + 8 * dgrp);
+    if (lane < HALF) {
+      float pa[GS + 1], pb[GS + 1];
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
+        pa[g] = bf16_to_f32(qr[ia]);
+        pb[g] = bf16_to_f32(qr[ib]);
+      }
+      const bf16_t* knr = reinterpret_cast<const bf16_t*>(r.k_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh;
+      pa[GS] = bf16_to_f32(knr[ia]);
+      pb[GS] = bf16_to_f32(knr[ib]);
+      float sn, cs;
+      angle_sincos((double)(L - 1) * r.theta[lane], &sn, &cs);
+#pragma unroll
+      for (int g = 0; g <= GS; ++g) {
+        float ra, rb;
+        rope_rotate_pair(pa[g], pb[g], sn, cs, ra, rb);
+        rows[wave][g][ia] = f32_to_bf16(ra);
+        rows[wave][g][ib] = f32_to_bf16(rb);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's rows landed
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int g = 0; g < GS; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qf[g][i] = *reinterpret_cast<const u32x4*>(&rows[wave][g][8 * (part + LPK * i)]);
+  } else {
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qf[g][i] = ld16(qr + 8 * (part + LPK * i));
+    }
+  }
+
+  auto compute = [&](u32x4 (&kf)[PASSES][4], u32x4 (&vf)[VLOADS], int kw) {
+    if (kw >= L) return;  // wave-uniform: no key of this wave in the chunk
+    if constexpr (ROPE) {
+      // Slot L - 1 comes from the turned row in LDS and v_new (only the
+      // pass holding it has a key index that clamps to L - 1); the first
+      // head subgroup writes the new token's k and v into the caches.
+      const u32x4* kn = reinterpret_cast<const u32x4*>(&rows[wave][GS][0]);
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps)
+        if (min(kw + ps * KPP + key_sub, L - 1) == L - 1)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kf[ps][i] = kn[part + LPK * i];
+#pragma unroll
+      for (int t = 0; t < VLOADS; ++t)
+        if (min(kw + t * KPI + kq, L - 1) == L - 1) vf[t] = vn;
+      if (hs == 0) {
+        bf16_t* kc = reinterpret_cast<bf16_t*>(r.k_cache) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh +
+                     (int64_t)(L - 1) * p.kv_ss;
+        bf16_t* vc = reinterpret_cast<bf16_t*>(r.v_cache) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh +
+                     (int64_t)(L - 1) * p.kv_ss;
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps)
+          if (kw + ps * KPP + key_sub == L - 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st16(kc + 8 * (part + LPK * i), kn[part + LPK * i]);
+#pragma unroll
+        for (int t = 0; t < VLOADS; ++t)
+          if (kw + t * KPI + kq == L - 1) st16(vc + 8 * dgrp, vn);
+      }
+    }
+    // ---- scores: z = scale * log2(e) * q.k ----
+    float z[GS][PASSES];
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const bool valid = kw + ps * KPP + key_sub < L;
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d = dot2(qf[g][i][e], kf[ps][i][e], d);
+        d = sum_within<LPK>(d);
+        z[g][ps] = valid ? d * c : -INFINITY;
+      }
+    }
+    // ---- running softmax: raise the max, rescale, add this chunk ----
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      float mx = z[g][0];
+#pragma unroll
+      for (int ps = 1; ps < PASSES; ++ps) mx = fmaxf(mx, z[g][ps]);
+      const float m_new = fmaxf(m_w[g], max_above<LPK>(mx));
+      const float a = exp2f(m_w[g] - m_new);  // 0 on the wave's first chunk
+      l_w[g] *= a;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] *= a;
+      m_w[g] = m_new;
+      float sm = 0.f;
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) {
+        z[g][ps] = exp2f(z[g][ps] - m_new);
+        sm += z[g][ps];
+      }
+      l_w[g] += sum_above<LPK>(sm);
+    }
+    if (part == 0) {
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) {
+        f32x4 pv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < GS; ++g) pv[g] = z[g][ps];
+        p_lds[wave][ps * KPP + key_sub] = pv;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes landed
+    __builtin_amdgcn_wave_barrier();
+    // ---- p.V, two keys' values of one d paired per packed dot product ----
+#pragma unroll
+    for (int t = 0; t < VLOADS; t += 2) {
+      const f32x4 pa = p_lds[wave][t * KPI + kq];
+      const f32x4 pb = p_lds[wave][(t + 1) * KPI + kq];
+      uint32_t pp[GS];
+#pragma unroll
+      for (int g = 0; g < GS; ++g) pp[g] = pack_bf16x2(pa[g], pb[g]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = __builtin_amdgcn_perm(vf[t + 1][e], vf[t][e], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(vf[t + 1][e], vf[t][e], 0x07060302u);
+#pragma unroll
+        for (int g = 0; g < GS; ++g) {
+          acc[g][2 * e] = dot2(pp[g], lo, acc[g][2 * e]);
+          acc[g][2 * e + 1] = dot2(pp[g], hi, acc[g][2 * e + 1]);
+        }
+      }
+    }
+  };
+
+  for (int kc = 0;;) {
+    compute(kf, vf, kc + wave * WK);
+    kc += KEYS;
+    if (kc >= L) break;
+    load(kf, vf, kc + wave * WK);
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
+  }
+
+  // ---- merge: the KPI key lanes of a wave by lane shuffles, then the W
+  // waves in LDS; final rows ----
+#pragma unroll
+  for (int g = 0; g < GS; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = sum_above<LPR>(acc[g][e]);
+  if (kq == 0) {
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      *reinterpret_cast<f32x4*>(&o_lds[wave][g][8 * dgrp]) = f32x4{acc[g][0], acc[g][1], acc[g][2], acc[g][3]};
+      *reinterpret_cast<f32x4*>(&o_lds[wave][g][8 * dgrp + 4]) = f32x4{acc[g][4], acc[g][5], acc[g][6], acc[g][7]};
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      ml_lds[wave][g][0] = m_w[g];
+      ml_lds[wave][g][1] = l_w[g];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < GS * D; i += 64 * W) {
+    const int g = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, ml_lds[w][g][0]);
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float f = exp2f(ml_lds[w][g][0] - M);  // 0 for a wave without keys
+      lsum = fmaf(ml_lds[w][g][1], f, lsum);
+      o = fmaf(o_lds[w][g][d], f, o);
+    }
+    const int h = h0 + g;
+    bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
+    orow[d] = f32_to_bf16(o / lsum);
+    if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + h] = (M + log2f(lsum)) * kLn2;
+  }
+}
+
 // Merge the chunks of one (sequence, query head): max-rescaled sums.
 template <int D>
 __global__ void __launch_bounds__(256) decode_combine_kernel(AttnParams p, DecodeWs ws) {
@@ -480,12 +757,47 @@ int chunk_mul(int B, int Hkv, int nsub, int D, int max_len) {
   return wgs >= 4 * 256 ? 2 : 1;
 }
 
+// The walking form: one query head per workgroup (so q and the output take
+// few registers), 64 keys per wave (32 at head dim 128), 12 waves (three per
+// SIMD, up to 168 registers each: the token's RoPE prologue does not spill).
+// Both variants take the same shape, so the step with RoPE inside stays bit
+// for bit the two-launch step.
+template <bool ROPE>
+constexpr int loop_waves() { return 12; }
+template <int D>
+constexpr int loop_mul() { return D == 128 ? 1 : 2; }
+template <int D, bool ROPE>
+constexpr int loop_keys() { return loop_waves<ROPE>() * Chunk<D, loop_mul<D>()>::WAVE_KEYS; }
+
+template <int D, bool ROPE>
+hipError_t launch_loop(const AttnParams& p, const DecodeRope& r, hipStream_t stream) {
+  const int nsub = p.Hq / p.Hkv;  // one query head per workgroup
+  const dim3 grid(1, p.Hkv * nsub, p.B), block(64 * loop_waves<ROPE>());
+  KernelTimer kt_("decode_loop_kernel", stream);
+  hipLaunchKernelGGL((decode_loop_kernel<D, 1, loop_mul<D>(), ROPE, loop_waves<ROPE>()>), grid, block, 0, stream,
+                     p, nsub, r);
+  return hipGetLastError();
+}
+
+// The walking form takes over when the split grid would not give every
+// compute unit a workgroup and a sequence needs at most kLoopPasses passes
+// of the walking workgroup (so its serial walk stays short).
+constexpr int kLoopPasses = 2;
+template <int D, bool ROPE>
+bool use_loop(const AttnParams& p, int nsub, int mul) {
+  const int64_t units = (int64_t)p.B * p.Hkv * nsub;
+  const int64_t split_wgs = units * ((p.max_len + chunk_keys(D, mul) - 1) / chunk_keys(D, mul));
+  const int passes = (p.max_len + loop_keys<D, ROPE>() - 1) / loop_keys<D, ROPE>();
+  return split_wgs <= 256 && passes <= kLoopPasses;
+}
+
 template <int D, bool ROPE>
 hipError_t launch_d(const AttnParams& p, const DecodeRope& r, DecodeWs ws, hipStream_t stream) {
   const int group = p.Hq / p.Hkv;
   const int gs = heads_per_wg(group);
   const int nsub = group / gs;
   const int mul = chunk_mul(p.B, p.Hkv, nsub, D, p.max_len);
+  if (use_loop<D, ROPE>(p, nsub, mul)) return launch_loop<D, ROPE>(p, r, stream);
   ws.chunk = chunk_keys(D, mul);
   ws.NS = (p.max_len + ws.chunk - 1) / ws.chunk;
   hipError_t e = mul == 2 ? launch_dm<D, 2, ROPE>(p, r, ws, gs, nsub, stream)

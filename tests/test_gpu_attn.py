@@ -114,6 +114,24 @@ def test_decode_bf16(case):
     assert (lse.cpu().double() - ref_lse).abs().max().item() < 1e-3
 
 
+@pytest.mark.parametrize("D,longest", [(32, 3072), (64, 1536), (128, 768)])
+def test_decode_walk_at_its_longest_and_split_one_key_past_it(D, longest):
+    # A small grid walks each sequence in one workgroup of 12 waves for up to
+    # two passes (12 x 128, 12 x 64 or 12 x 32 keys per pass at head dim 32,
+    # 64, 128); one key more takes the split-K kernel and its merge.  Both
+    # against the oracle, and against each other.
+    Hq, Hkv = 8, 2
+    lens = [longest, longest // 2 + 1, 256, 1]
+    q, kc, vc, L = _decode_case(len(lens), Hq, Hkv, D, lens, longest + 1, torch.bfloat16, 77 + D)
+    ref = oracle.attn_decode(q, kc, vc, L)
+    qg, kg, vg, Lg = q.cuda(), kc.cuda(), vc.cuda(), L.cuda()
+    walk = rgc.gqa_attn_decode(qg, kg, vg, Lg, longest)
+    split = rgc.gqa_attn_decode(qg, kg, vg, Lg, longest + 1)
+    assert_close(walk, ref, torch.bfloat16, "decode walk, 8 chunks")
+    assert_close(split, ref, torch.bfloat16, "decode split, 2049 keys")
+    assert (walk.float() - split.float()).abs().max().item() <= 2.0 ** -6
+
+
 def test_decode_fp32():
     q, kc, vc, L = _decode_case(3, 4, 2, 32, [1, 17, 24], 24, torch.float32, 3)
     ref = oracle.attn_decode(q, kc, vc, L)
@@ -136,8 +154,9 @@ def test_prefill_and_decode_when_the_running_max_rises_tile_after_tile(dtype, D,
     # units of the scaled score) every 64 keys, so almost every later tile
     # holds a new row maximum -- for the bf16 kernels, past their rescale
     # threshold of 2^8 (5.5 score units): the rare raise-and-rescale path
-    # runs on most tiles of most rows, in prefill and in the split-K decode
-    # and its combine.  The fp32 case grows more slowly: scores rounded in
+    # runs on most tiles of most rows, in prefill and in both decode forms
+    # (the one-workgroup walk, which rescales across its chunks, at batch 1;
+    # the split-K kernel and its merge with the batch repeated 64 times).  The fp32 case grows more slowly: scores rounded in
     # fp32 carry an error of |s| 2^-24, which logits of ~65 would lift past
     # the 1e-5 bar through the exponentials; at ~16 they stay well inside.
     B, S, Hq, Hkv = 1, 520, 4, 2
@@ -163,6 +182,11 @@ def test_prefill_and_decode_when_the_running_max_rises_tile_after_tile(dtype, D,
     ref1 = oracle.attn_decode(q1, kc, vc, lens)
     o1 = rgc.gqa_attn_decode(q1.cuda(), kc.cuda(), vc.cuda(), lens.cuda(), S)
     assert_close(o1, ref1, dtype, "decode, rising scores")
+    if dtype == torch.bfloat16:
+        R = 64
+        o64 = rgc.gqa_attn_decode(q1.repeat(R, 1, 1).cuda(), kc.repeat(R, 1, 1, 1).cuda(), vc.repeat(R, 1, 1, 1).cuda(),
+                                  lens.repeat(R).cuda(), S)
+        assert_close(o64, ref1.repeat(R, 1, 1), dtype, "split-K decode, rising scores")
 
 
 def test_decode_equals_prefill_last_row_and_gqa_equals_mha_on_gpu():
