@@ -402,8 +402,8 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
 // waves then merge in LDS and write the final row: no partials and no merge
 // launch.  Used where the split kernel's chunks could not fill the chip
 // anyway (a few sequences, as in batch-1 generation), so its second launch
-// would dominate the step; with 16 waves a sequence of up to 512 or 1024
-// keys takes a single pass.
+// would dominate the step.  With 12 waves one pass covers 384, 768 or 1536
+// keys at head dim 128, 64 or 32.
 template <int D, int GS, int MUL, bool ROPE, int W>
 __global__ void __launch_bounds__(64 * W) decode_loop_kernel(AttnParams p, int nsub, DecodeRope r) {
   constexpr int WK = Chunk<D, MUL>::WAVE_KEYS;
