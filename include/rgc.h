@@ -208,8 +208,9 @@ int rgc_norm_rope_append(void* q, const void* k_new, const void* v_new, void* k_
  * o[b,s,h,:] = sum_{j<=p} softmax_j(scale * q . K_j) V_j with KV head
  * h / (Hq/Hkv).  bf16: scores, softmax and accumulation in fp32, the
  * probabilities rounded to bf16 for the second product, the output rounded
- * to nearest even.  A sequence whose q_start puts a row outside [0, S_max)
- * gets NaN rows and a flag.
+ * to nearest even.  bf16: the token stride kv_ss must lie in [0, 2^24)
+ * elements (RGC_ERR_LAYOUT otherwise).  A sequence whose q_start puts a row
+ * outside [0, S_max) gets NaN rows and a flag.
  */
 int rgc_gqa_attn_prefill(void* o, const void* q, const void* k_cache,
                          const void* v_cache, int dtype, int B, int Sq, int Hq,
@@ -234,7 +235,8 @@ int rgc_gqa_attn_prefill(void* o, const void* q, const void* k_cache,
  *              at most T).
  *   max_seqlen host: the longest document (sizes the launch).
  *   lse        [Hq,T] fp32 or NULL.
- * bf16 only; head dim 32, 64 or 128.  Offsets that are decreasing, exceed T
+ * bf16 only; head dim 32, 64 or 128; kv_ts in [0, 2^24) elements
+ * (RGC_ERR_LAYOUT otherwise).  Offsets that are decreasing, exceed T
  * or give a document longer than max_seqlen raise *err_flag and that
  * document is not computed.  Same arithmetic as rgc_gqa_attn_prefill.
  */
@@ -289,7 +291,8 @@ int rgc_gqa_attn_backward(void* dq, void* dk, void* dv, const void* q, const voi
  *   lambda     the constant weight of the second map (no re-normalisation).
  *   scale      applied to both maps' scores (1/sqrt(D) is the usual value).
  * bf16 only (RGC_ERR_DTYPE otherwise); D must be 64, the head dim of each
- * map in the differential workload (RGC_ERR_HEADDIM otherwise).  Each map is normalised by the sum of the bf16-rounded
+ * map in the differential workload (RGC_ERR_HEADDIM otherwise); kv_ss in
+ * [0, 2^24) elements (RGC_ERR_LAYOUT otherwise).  Each map is normalised by the sum of the bf16-rounded
  * weights it multiplies V with; o is rounded once from fp32.  A row whose
  * slots fall outside the cache gets NaN and raises *err_flag.
  */

@@ -24,6 +24,11 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // Strides in elements must keep every row start on a 16-byte boundary.
 bool stride_ok(int64_t s, int dt) { return (s * esize(dt)) % 16 == 0; }
 
+// The bf16 matrix-core kernels stage a tile's rows at 32-bit byte offsets
+// from the tile's first row (up to 63 token strides of 2 bytes): a token
+// stride in [0, 2^24) elements keeps every such offset below 2^31.
+bool token_stride_ok(int64_t s) { return s >= 0 && s < (int64_t(1) << 24); }
+
 int hip_status(hipError_t e) { return e == hipSuccess ? RGC_OK : RGC_ERR_HIP; }
 
 }  // namespace
@@ -225,6 +230,7 @@ int rgc_gqa_attn_prefill(void* o, const void* q, const void* k_cache, const void
       !stride_ok(o_sb, dtype) || !stride_ok(o_ss, dtype) || !stride_ok(o_sh, dtype) ||
       !stride_ok(kv_sb, dtype) || !stride_ok(kv_sh, dtype) || !stride_ok(kv_ss, dtype))
     return RGC_ERR_LAYOUT;
+  if (dtype == RGC_BF16 && !token_stride_ok(kv_ss)) return RGC_ERR_LAYOUT;
   if ((int64_t)B * Sq * Hq > 0x7FFFFFFFLL) return RGC_ERR_SHAPE;
   AttnParams p = {};
   p.o = o;
@@ -271,6 +277,7 @@ int rgc_gqa_attn_prefill_varlen(void* o, const void* q, const void* k, const voi
   if (!stride_ok(q_ts, dtype) || !stride_ok(q_hs, dtype) || !stride_ok(o_ts, dtype) || !stride_ok(o_hs, dtype) ||
       !stride_ok(kv_ts, dtype) || !stride_ok(kv_hs, dtype))
     return RGC_ERR_LAYOUT;
+  if (!token_stride_ok(kv_ts)) return RGC_ERR_LAYOUT;
   if ((int64_t)n_docs * Hq * ((max_seqlen + 255) / 256) > 0x7FFFFFFFLL) return RGC_ERR_SHAPE;
   AttnParams p = {};
   p.o = o;
@@ -376,6 +383,7 @@ int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2, const void* k
       !stride_ok(o_sb, dtype) || !stride_ok(o_ss, dtype) || !stride_ok(o_sh, dtype) ||
       !stride_ok(kv_sb, dtype) || !stride_ok(kv_sh, dtype) || !stride_ok(kv_ss, dtype))
     return RGC_ERR_LAYOUT;
+  if (!token_stride_ok(kv_ss)) return RGC_ERR_LAYOUT;
   if ((int64_t)B * Sq * Hq > 0x7FFFFFFFLL) return RGC_ERR_SHAPE;
   DiffParams dp = {};
   AttnParams& p = dp.a;

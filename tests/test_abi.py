@@ -63,6 +63,8 @@ def test_prefill_rejects_bad_arguments_before_launch():
     assert _prefill(q=None) == NULL
     assert _prefill(o=A + 2) == LAYOUT
     assert _prefill(q_ss=4 * 128 + 1) == LAYOUT
+    assert _prefill(kv_ss=1 << 24) == LAYOUT       # bf16 token stride past 2^24 elements
+    assert _prefill(kv_ss=-128) == LAYOUT
     assert _prefill(Sq=17) == CAPACITY
     assert _prefill(scale=float("nan")) == -10
     assert _prefill(B=0) == OK                      # empty batch: a no-op
@@ -86,6 +88,7 @@ def test_diff_rejects_bad_arguments_before_launch():
     assert _diff(D=128) == HEADDIM       # head dim 64 only
     assert _diff(q2=None) == NULL
     assert _diff(k2=A + 8) == LAYOUT
+    assert _diff(kv_ss=1 << 24) == LAYOUT
     assert _diff(Sq=17) == CAPACITY
     assert _diff(lam=float("inf")) == -10
     assert _diff(B=0) == OK
@@ -108,6 +111,7 @@ def test_varlen_rejects_bad_arguments_before_launch():
     assert _varlen(cu=None) == NULL
     assert _varlen(maxlen=41) == CAPACITY
     assert _varlen(kv_ts=127) == LAYOUT
+    assert _varlen(kv_ts=1 << 24) == LAYOUT
     assert _varlen(n=0) == OK
     assert _varlen(T=0, maxlen=0) == OK
 
