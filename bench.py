@@ -4,10 +4,11 @@ One step = one pass of the whole path over one batch of synthetic input:
   prefill phase  (24 query / 8 KV heads, head dim 128, batch 8 x 2048 tokens):
                  fused RoPE on q and k + cache append, causal GQA prefill;
   decode phase   (64 sequences, cache lengths uniform on {256..2048}, same
-                 heads): 32 generation steps of fused RoPE on the new q and
-                 k + cache append, then cached GQA decode (the lengths of
-                 every step are precomputed once, as a serving loop knows
-                 them).
+                 heads): 32 generation steps, each one launch of the cached
+                 GQA decode with the new token's RoPE (q and k) and the
+                 append of its k and v inside, plus the chunk merge (the
+                 lengths of every step are precomputed once, as a serving
+                 loop knows them).
 `value` is the decode phase's KV-read rate (cache bytes every decode call
 must read / decode-phase time, GB/s); the prefill phase's attention rate is
 reported beside it (TFLOP/s over unmasked query-key pairs).  Both are also
@@ -496,7 +497,7 @@ def main():
 
     for i in range(args.warmup):
         pre.run(False)
-        dec.run()
+        dec.run(fused=True)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
@@ -520,7 +521,7 @@ def main():
         last = i == args.steps - 1
         if last:
             rgc.timing_enable(True)
-        dec.run()
+        dec.run(fused=True)
         if last:
             rgc.timing_enable(False)
         z.record()

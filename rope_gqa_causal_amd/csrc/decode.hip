@@ -187,25 +187,30 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
     // to -inf, so they weigh nothing.
     u32x4 qf[GS][4];
     // With ROPE, lane m < D/2 instead loads pair m (elements ia, ib) of each
-    // q row and, in the last chunk, of the new k; it turns them below and
-    // the rows reach the q.k layout through LDS.
+    // q row and of the new k (and every lane its piece of the new v); it
+    // turns them below and the rows reach the q.k layout through LDS.  These
+    // loads, and the lane's theta, go out first and unconditionally (lanes
+    // past D/2 read pair 0 and ignore it), and their values are only used
+    // after the K and V loads are issued: a wait for them then never waits
+    // for K or V.
     constexpr int HALF = D / 2;
-    const int ia = r.style == ROPE_HALF ? lane : 2 * lane, ib = r.style == ROPE_HALF ? lane + HALF : 2 * lane + 1;
-    float pa[GS + 1], pb[GS + 1];
+    const int lm = lane < HALF ? lane : 0;
+    const int ia = r.style == ROPE_HALF ? lm : 2 * lm, ib = r.style == ROPE_HALF ? lm + HALF : 2 * lm + 1;
+    bf16_t qa[GS + 1], qb[GS + 1];
+    double theta = 0.0;
+    u32x4 kn[4] = {}, vn = {};  // the new token's rotated k and its v (last chunk)
     if constexpr (ROPE) {
-      if (lane < HALF) {
+      theta = r.theta[lm];
 #pragma unroll
-        for (int g = 0; g < GS; ++g) {
-          const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
-          pa[g] = bf16_to_f32(qr[ia]);
-          pb[g] = bf16_to_f32(qr[ib]);
-        }
-        if (last) {
-          const bf16_t* knr = reinterpret_cast<const bf16_t*>(r.k_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh;
-          pa[GS] = bf16_to_f32(knr[ia]);
-          pb[GS] = bf16_to_f32(knr[ib]);
-        }
+      for (int g = 0; g < GS; ++g) {
+        const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
+        qa[g] = qr[ia];
+        qb[g] = qr[ib];
       }
+      const bf16_t* knr = reinterpret_cast<const bf16_t*>(r.k_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh;
+      qa[GS] = knr[ia];
+      qb[GS] = knr[ib];
+      vn = ld16(reinterpret_cast<const bf16_t*>(r.v_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh + 8 * dgrp);
     } else {
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
@@ -227,11 +232,6 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
       const int key = min(kw + t * KPI + kq, L - 1);
       vf[t] = ld16(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
     }
-    u32x4 kn[4] = {}, vn = {};  // the new token's rotated k and its v (last chunk)
-    if constexpr (ROPE) {
-      if (last)
-        vn = ld16(reinterpret_cast<const bf16_t*>(r.v_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh + 8 * dgrp);
-    }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
 
     if constexpr (ROPE) {
@@ -241,12 +241,12 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
       __shared__ __attribute__((aligned(16))) bf16_t rows[kWaves][GS + 1][D];
       if (lane < HALF) {
         float sn, cs;
-        angle_sincos((double)(L - 1) * r.theta[lane], &sn, &cs);
+        angle_sincos((double)(L - 1) * theta, &sn, &cs);
 #pragma unroll
         for (int g = 0; g <= GS; ++g) {
           if (g == GS && !last) break;
           float ra, rb;
-          rope_rotate_pair(pa[g], pb[g], sn, cs, ra, rb);
+          rope_rotate_pair(bf16_to_f32(qa[g]), bf16_to_f32(qb[g]), sn, cs, ra, rb);
           rows[wave][g][ia] = f32_to_bf16(ra);
           rows[wave][g][ib] = f32_to_bf16(rb);
         }
