@@ -471,38 +471,49 @@ __global__ void __launch_bounds__(64 * W) decode_loop_kernel(AttnParams p, int n
       vf[t] = ld16(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
     }
   };
-  // The first pass's K and V loads go out before q's, so the q prologue
-  // (with ROPE: the angle, the rotation and the LDS round trip) runs while
-  // they are in flight.
+  // q (with ROPE: the lane's theta, the q and new-k pairs -- lanes past D/2
+  // read pair 0 and ignore it -- and its piece of the new v) is loaded
+  // first, then the first pass's K and V; the pairs are converted and turned
+  // only after those loads are issued, so a wait for them never waits for K
+  // or V, and the rotation (the RoPE kernels' angle, rotation and rounding,
+  // through this wave's LDS rows) runs under the cache loads.
+  u32x4 qf[GS][4];
+  u32x4 vn = {};
+  const int lm = lane < HALF ? lane : 0;
+  const int ia = r.style == ROPE_HALF ? lm : 2 * lm, ib = r.style == ROPE_HALF ? lm + HALF : 2 * lm + 1;
+  bf16_t qa[GS + 1], qb[GS + 1];
+  double theta = 0.0;
+  if constexpr (ROPE) {
+    theta = r.theta[lm];
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
+      qa[g] = qr[ia];
+      qb[g] = qr[ib];
+    }
+    const bf16_t* knr = reinterpret_cast<const bf16_t*>(r.k_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh;
+    qa[GS] = knr[ia];
+    qb[GS] = knr[ib];
+    vn = ld16(reinterpret_cast<const bf16_t*>(r.v_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh + 8 * dgrp);
+  } else {
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qf[g][i] = ld16(qr + 8 * (part + LPK * i));
+    }
+  }
   u32x4 kf[PASSES][4], vf[VLOADS];
   load(kf, vf, wave * WK);
   __builtin_amdgcn_sched_barrier(0);
-
-  // ---- q in the q.k layout; with ROPE, q and the new token's k turned at
-  // position L - 1 through this wave's LDS rows (the RoPE kernels' angle,
-  // rotation and rounding), and the new token's v ----
-  u32x4 qf[GS][4];
-  u32x4 vn = {};
   if constexpr (ROPE) {
-    const int ia = r.style == ROPE_HALF ? lane : 2 * lane, ib = r.style == ROPE_HALF ? lane + HALF : 2 * lane + 1;
-    vn = ld16(reinterpret_cast<const bf16_t*>(r.v_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh + 8 * dgrp);
     if (lane < HALF) {
-      float pa[GS + 1], pb[GS + 1];
-#pragma unroll
-      for (int g = 0; g < GS; ++g) {
-        const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
-        pa[g] = bf16_to_f32(qr[ia]);
-        pb[g] = bf16_to_f32(qr[ib]);
-      }
-      const bf16_t* knr = reinterpret_cast<const bf16_t*>(r.k_new) + (int64_t)b * r.n_sb + (int64_t)kvh * r.n_sh;
-      pa[GS] = bf16_to_f32(knr[ia]);
-      pb[GS] = bf16_to_f32(knr[ib]);
       float sn, cs;
-      angle_sincos((double)(L - 1) * r.theta[lane], &sn, &cs);
+      angle_sincos((double)(L - 1) * theta, &sn, &cs);
 #pragma unroll
       for (int g = 0; g <= GS; ++g) {
         float ra, rb;
-        rope_rotate_pair(pa[g], pb[g], sn, cs, ra, rb);
+        rope_rotate_pair(bf16_to_f32(qa[g]), bf16_to_f32(qb[g]), sn, cs, ra, rb);
         rows[wave][g][ia] = f32_to_bf16(ra);
         rows[wave][g][ib] = f32_to_bf16(rb);
       }
@@ -513,13 +524,6 @@ __global__ void __launch_bounds__(64 * W) decode_loop_kernel(AttnParams p, int n
     for (int g = 0; g < GS; ++g)
 #pragma unroll
       for (int i = 0; i < 4; ++i) qf[g][i] = *reinterpret_cast<const u32x4*>(&rows[wave][g][8 * (part + LPK * i)]);
-  } else {
-#pragma unroll
-    for (int g = 0; g < GS; ++g) {
-      const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (int64_t)(h0 + g) * p.q_sh;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qf[g][i] = ld16(qr + 8 * (part + LPK * i));
-    }
   }
 
   auto compute = [&](u32x4 (&kf)[PASSES][4], u32x4 (&vf)[VLOADS], int kw) {
