@@ -131,10 +131,10 @@ def summarize_pmc(fetch_dir, write_dir):
             f.write("\n")
         print(kind, json.dumps(rec))
     record("decode", "decode.hip", ["decode_split_kernel"],
-           "the decode's dominant kernel, average over the 32 decode calls of one bench step "
-           "(cache lengths grow by one per call)")
+           "the decode's dominant kernel (with the token's RoPE and append inside), average over the 32 "
+           "decode calls of one bench step (cache lengths grow by one per call)")
     record("decode_op", "decode.hip", ["decode_split_kernel", "decode_combine_kernel"],
-           "the whole decode op (split + merge), average over the 32 decode calls of one bench step")
+           "the whole one-launch decode step (split + merge), average over the 32 decode calls of one bench step")
     record("prefill", "prefill.hip", ["prefill_kernel"], "one prefill launch of the bench step")
 
 
@@ -582,7 +582,8 @@ def main():
         "decode_phase_ms_per_step": round(dec_ms / args.steps, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split_kernel (the decode's dominant kernel: streams the cache)",
+            "kernel": "decode_split_kernel with the token's RoPE and append inside (the decode's dominant "
+                      "kernel: streams the cache)",
             "achieved": round(dec_achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -591,7 +592,7 @@ def main():
             "algorithmic_bytes_per_launch": round(dk_bytes_avg),
             "avg_launch_us": round(dk_avg * 1e3, 3),
             "op": {
-                "kernels": "decode_split_kernel + decode_combine_kernel (gqa_attn_decode)",
+                "kernels": "decode_split_kernel + decode_combine_kernel (gqa_attn_decode_rope_append)",
                 "avg_kernel_us": round(op_avg * 1e3, 3),
                 "achieved": round(op_achieved, 2),
                 "frac": round(op_achieved / HBM_PEAK_GBS, 4),
