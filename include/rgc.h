@@ -22,7 +22,9 @@
  * Conventions shared by every entry point:
  *  - Every data pointer is a DEVICE pointer (HIP global memory) unless the
  *    argument says "host".  The caller owns every buffer; the library never
- *    allocates, frees or synchronises and keeps no mutable global state.
+ *    allocates, frees or synchronises and keeps no mutable global state,
+ *    except for the opt-in per-kernel timing (rgc_timing_enable /
+ *    rgc_timing_report), which creates HIP events and waits for them.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns.
  *  - Shapes are element counts; strides are in ELEMENTS, not bytes.  The
