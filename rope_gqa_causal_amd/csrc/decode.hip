@@ -682,7 +682,9 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(AttnParams p, Decod
   constexpr int EPL = D >= 64 ? D / 64 : 1;  // output elements per lane
   constexpr int kPre = 16;
   const int lane = threadIdx.x & 63;
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // The (sequence, head) index is wave-uniform: through readfirstlane it
+  // lives in a scalar register, so its length comes by a scalar load.
+  const int bh = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (bh >= p.B * p.Hq) return;
   const int b = bh / p.Hq, h = bh % p.Hq;
   const int L = p.seq_lens[b];
