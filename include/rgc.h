@@ -45,6 +45,9 @@
  *  - Query head h reads KV head h / (Hq / Hkv); Hq must be a multiple of
  *    Hkv (RGC_ERR_GROUP otherwise).
  *  - Supported head dims: 32, 64, 128 (RGC_ERR_HEADDIM otherwise).
+ *  - Every attention entry point takes a softmax `scale` that must be
+ *    positive and finite (RGC_ERR_ARG otherwise): the causal mask is the
+ *    -inf score that a positive scale leaves at -inf.
  */
 #ifndef RGC_H
 #define RGC_H

@@ -223,7 +223,7 @@ int rgc_gqa_attn_prefill(void* o, const void* q, const void* k_cache, const void
   if (B == 0 || Sq == 0) return RGC_OK;
   if (!o || !q || !k_cache || !v_cache) return RGC_ERR_NULL;
   if (Sq > S_max) return RGC_ERR_CAPACITY;
-  if (!std::isfinite(scale)) return RGC_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return RGC_ERR_ARG;
   if (!aligned16(o) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return RGC_ERR_LAYOUT;
   if (!stride_ok(q_sb, dtype) || !stride_ok(q_ss, dtype) || !stride_ok(q_sh, dtype) ||
@@ -272,7 +272,7 @@ int rgc_gqa_attn_prefill_varlen(void* o, const void* q, const void* k, const voi
   if (n_docs == 0 || max_seqlen == 0 || total_tokens == 0) return RGC_OK;
   if (!o || !q || !k || !v || !cu_seqlens) return RGC_ERR_NULL;
   if (max_seqlen > total_tokens) return RGC_ERR_CAPACITY;
-  if (!std::isfinite(scale)) return RGC_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return RGC_ERR_ARG;
   if (!aligned16(o) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return RGC_ERR_LAYOUT;
   if (!stride_ok(q_ts, dtype) || !stride_ok(q_hs, dtype) || !stride_ok(o_ts, dtype) || !stride_ok(o_hs, dtype) ||
       !stride_ok(kv_ts, dtype) || !stride_ok(kv_hs, dtype))
@@ -324,7 +324,7 @@ int rgc_gqa_attn_backward(void* dq, void* dk, void* dv, const void* q, const voi
   if (dtype != RGC_BF16) return RGC_ERR_DTYPE;
   if (B == 0 || S == 0) return RGC_OK;
   if (!dq || !dk || !dv || !q || !k || !v || !o || !d_o || !lse) return RGC_ERR_NULL;
-  if (!std::isfinite(scale)) return RGC_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return RGC_ERR_ARG;
   if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
       !aligned16(o) || !aligned16(d_o))
     return RGC_ERR_LAYOUT;
@@ -375,7 +375,7 @@ int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2, const void* k
   if (B == 0 || Sq == 0) return RGC_OK;
   if (!o || !q1 || !q2 || !k1_cache || !k2_cache || !v_cache) return RGC_ERR_NULL;
   if (Sq > S_max) return RGC_ERR_CAPACITY;
-  if (!std::isfinite(scale) || !std::isfinite(lambda)) return RGC_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale) || !std::isfinite(lambda)) return RGC_ERR_ARG;
   if (!aligned16(o) || !aligned16(q1) || !aligned16(q2) || !aligned16(k1_cache) || !aligned16(k2_cache) ||
       !aligned16(v_cache))
     return RGC_ERR_LAYOUT;
@@ -434,7 +434,7 @@ int rgc_gqa_attn_decode(void* o, const void* q, const void* k_cache, const void*
   if (B == 0) return RGC_OK;
   if (!o || !q || !k_cache || !v_cache || !seq_lens) return RGC_ERR_NULL;
   if (max_len < 1 || max_len > S_max) return RGC_ERR_CAPACITY;
-  if (!std::isfinite(scale)) return RGC_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return RGC_ERR_ARG;
   if (!aligned16(o) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return RGC_ERR_LAYOUT;
   if (!stride_ok(q_sb, dtype) || !stride_ok(q_sh, dtype) || !stride_ok(o_sb, dtype) ||
@@ -490,7 +490,7 @@ int rgc_gqa_attn_decode_rope_append(void* o, const void* q, const void* k_new, c
   if (B == 0) return RGC_OK;
   if (!o || !q || !k_new || !v_new || !k_cache || !v_cache || !seq_lens) return RGC_ERR_NULL;
   if (max_len < 1 || max_len > S_max) return RGC_ERR_CAPACITY;
-  if (!std::isfinite(scale)) return RGC_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return RGC_ERR_ARG;
   if (!aligned16(o) || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
       !aligned16(v_cache))
     return RGC_ERR_LAYOUT;

@@ -246,3 +246,17 @@ def test_timing_switch_and_empty_report():
     assert lib.rgc_timing_report(buf, len(buf)) == 0 and buf.value == b""
     assert lib.rgc_timing_report(None, 16) == -10  # RGC_ERR_ARG
     assert lib.rgc_timing_report(buf, 0) == -10
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+def test_attention_entries_reject_a_scale_that_is_not_positive_and_finite(scale):
+    # The bf16 kernels mask a score by setting it to -inf before it is
+    # multiplied by the scale, which is only the mask a positive scale needs;
+    # every attention entry therefore takes the same rule: scale > 0, finite.
+    assert _prefill(scale=scale) == ARG
+    assert _prefill(scale=scale, dt=F32) == ARG
+    assert _diff(scale=scale) == ARG
+    assert _varlen(scale=scale) == ARG
+    assert _bwd(scale=scale) == ARG
+    assert _decode(scale=scale) == ARG
+    assert _decode_rope(scale=scale) == ARG
