@@ -8,21 +8,26 @@ One step = one pass of the whole path over one batch of synthetic input:
                  GQA decode with the new token's RoPE (q and k) and the
                  append of its k and v inside, plus the chunk merge (the
                  lengths of every step are precomputed once, as a serving
-                 loop knows them).
+                 loop knows them).  Successive decode calls rotate over
+                 several independent cache sets (3 by default, 545 MB each),
+                 so no call finds the cache rows of the previous one in the
+                 256 MB last-level (MALL) cache: the rate is HBM bandwidth.
 `value` is the decode phase's KV-read rate (cache bytes every decode call
 must read / decode-phase time, GB/s); the prefill phase's attention rate is
-reported beside it (TFLOP/s over unmasked query-key pairs).  Both are also
-given per kernel against the MI355X peaks (HBM 8 TB/s; dense bf16 MFMA
-2.5 PFLOP/s), from HIP events recorded on the stream the kernels run on: the
-decode's dominant kernel (the split-K kernel that streams the cache) is timed
-by the library's per-kernel events, and the whole decode op (split + merge)
-is reported beside it.
+reported beside it (TFLOP/s over unmasked query-key pairs).  `roofline` is
+the whole decode op (split kernel + merge kernel) per call, from HIP events
+recorded around each decode call of the last timed step on the stream the
+library launches on; the split kernel alone is reported beside it, timed by
+the instrumented build of the library in an extra, untimed decode phase.
+`roofline_prefill` is the prefill kernel against the bf16 MFMA peak.
 The differential-attention variant (`diff_attn`), the packed-document prefill
 (`varlen_prefill`), the fused prologue with and without QK normalisation
-(`prologue`), the attention backward (`backward`) and the 125M-shaped cached
-versus recomputed generation (`generation_125m`) are timed apart on their own
-workloads.  The fp64 CPU oracle is timed on a bounded sample of the same
-decode workload.
+(`prologue`), the attention backward (`backward`), the 125M-shaped cached
+versus recomputed generation (`generation_125m`), a decode length sweep with
+a linear fit of time against cache length (`decode_length_sweep`) and the
+measured ceilings of this GPU (`ceilings`: a streaming read, a matrix-core
+loop) are timed apart on their own workloads.  The fp64 CPU oracle is timed
+on bounded samples of the decode and prefill workloads (`cpu_baseline`).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -50,12 +55,21 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="target wall time of each CPU-oracle sample (decode, prefill)")
+    ap.add_argument("--cache-sets", type=int, default=3,
+                    help="independent decode cache sets rotated call by call (1 = no rotation)")
+    ap.add_argument("--phase", choices=("all", "prefill", "decode"), default="all",
+                    help="time only one phase (for counter runs); the JSON line then carries that phase only")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the variant lines (diff, varlen, prologue, backward, generation)")
+                    help="skip the variant lines (diff, varlen, prologue, backward, generation, sweep, ceilings)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
+    ap.add_argument("--with-ceilings", action="store_true",
+                    help="run the ceiling kernels even with --no-extras (counter calibration runs)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="RUN_DIR",
+                    help="turn rocprofv3 --pmc runs of `--phase prefill --with-ceilings` into "
+                         "profiles/counters_prefill_mfma.json and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE; both "
                          "with --copy-calibration) into profiles/counters_*.json and exit")
@@ -78,6 +92,20 @@ def stored_traffic(kind, src, launches_bytes):
     if rec.get("kernel_sha") != kernel_sha(src):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def stored_mfma_util():
+    """Matrix-core utilisation of the prefill kernel from committed counter
+    runs, if the kernel is unchanged since they were taken."""
+    path = os.path.join(PROFILES, "counters_prefill_mfma.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("kernel_sha") != kernel_sha("prefill.hip"):
+        return None
+    return rec.get("derived")
 
 
 def _pmc_per_dispatch(run_dir, counter):
@@ -138,6 +166,61 @@ def summarize_pmc(fetch_dir, write_dir):
     record("prefill", "prefill.hip", ["prefill_kernel"], "one prefill launch of the bench step")
 
 
+def summarize_counters(run_dirs):
+    """Per-dispatch averages of every counter found in the rocpd databases of
+    the given runs, for the prefill kernel and for the matrix-core loop of
+    ceilings/ceilings.hip (the calibration: a kernel that does nothing but
+    back-to-back MFMA), and the ratios derived from them:
+      mfma_busy   SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs)
+                  (the usual MFMA-utilisation formula), beside the same
+                  figure for the calibration loop;
+      executed_flops  SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (flops per MOP);
+      valu_per_mfma   SQ_INSTS_VALU / SQ_INSTS_MFMA (when both were taken);
+      lds_conflict    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    per = {}
+    for d in run_dirs:
+        import glob
+        import sqlite3
+        for path in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+            rows = sqlite3.connect(path).execute(
+                "select dispatch_id, kernel_name, counter_name, value from counters_collection").fetchall()
+            for did, kname, cname, val in rows:
+                short = kname.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                short = short.split("<")[0].split("::")[-1]
+                if short not in ("prefill_kernel", "mfma_bf16_kernel"):
+                    continue
+                key = (path, did)
+                per.setdefault(short, {}).setdefault(cname, {}).setdefault(key, 0.0)
+                per[short][cname][key] += val
+    avg = {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+    pre = avg.get("prefill_kernel", {})
+    cal = avg.get("mfma_bf16_kernel", {})
+
+    def busy(a):
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in a and a.get("GRBM_GUI_ACTIVE"):
+            return a["SQ_VALU_MFMA_BUSY_CYCLES"] / (a["GRBM_GUI_ACTIVE"] * 256 * 4)
+        return None
+    derived = {"mfma_busy": busy(pre), "mfma_busy_calibration_loop": busy(cal)}
+    if derived["mfma_busy"] is not None and derived["mfma_busy_calibration_loop"]:
+        derived["mfma_busy_vs_loop"] = derived["mfma_busy"] / derived["mfma_busy_calibration_loop"]
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in pre:
+        derived["executed_mfma_flops"] = pre["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    if pre.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in pre:
+        derived["valu_per_mfma"] = pre["SQ_INSTS_VALU"] / pre["SQ_INSTS_MFMA"]
+    if pre.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in pre:
+        derived["lds_conflict_per_active"] = pre["SQ_LDS_BANK_CONFLICT"] / pre["SQ_LDS_IDX_ACTIVE"]
+    derived = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in derived.items()}
+    rec = {"kernel": "prefill_kernel", "kernel_sha": kernel_sha("prefill.hip"),
+           "counters_per_dispatch": {k: round(v, 1) for k, v in sorted(pre.items())},
+           "calibration_loop_counters_per_dispatch": {k: round(v, 1) for k, v in sorted(cal.items())},
+           "derived": derived,
+           "runs": [os.path.relpath(d, ROOT) for d in run_dirs]}
+    with open(os.path.join(PROFILES, "counters_prefill_mfma.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 class Prefill:
     def __init__(self, rgc, synth):
         w = synth.WORKLOADS["prefill3p8b"]
@@ -167,7 +250,7 @@ class Prefill:
 
 
 class Decode:
-    def __init__(self, rgc, synth):
+    def __init__(self, rgc, synth, cache_sets=3):
         w = synth.WORKLOADS["ragged_decode"]
         self.w = w
         g = synth.generator(w.seed)
@@ -175,7 +258,12 @@ class Decode:
         self.S_max = w.len_hi + w.steps
         kc, vc = synth.filled_cache(w.B, w.Hkv, self.S_max, w.D, g, w.dtype)
         self.kc_cpu, self.vc_cpu = kc, vc
-        self.kc, self.vc = kc.cuda(), vc.cuda()
+        # Independent cache sets at their own addresses, rotated call by call:
+        # a set is read again only after (sets - 1) other calls have streamed
+        # about 289 MB each through the 256 MB MALL.
+        first = (kc.cuda(), vc.cuda())
+        self.sets = [first] + [(first[0].clone(), first[1].clone()) for _ in range(max(cache_sets, 1) - 1)]
+        self.calls = 0
         q, k, v = synth.qkv(w.B * w.steps, 1, w.Hq, w.Hkv, w.D, g, w.dtype)
         self.q = q.view(w.steps, w.B, 1, w.Hq, w.D).cuda()
         self.k = k.view(w.steps, w.B, 1, w.Hkv, w.D).cuda()
@@ -193,20 +281,138 @@ class Decode:
         per_token = w.Hkv * w.D * 2 * 2
         self.bytes_per_call = [per_token * float((self.lens0_cpu + t + 1).sum()) for t in range(w.steps)]
 
-    def run(self, fused=False):
+    def run(self, fused=True, events=None):
+        """The 32 decode calls of one step; with ``events`` (a list), each call
+        is bracketed by HIP events on the current stream (the library's)."""
         r, w = self.rgc, self.w
         for t in range(w.steps):
+            kc, vc = self.sets[self.calls % len(self.sets)]
+            self.calls += 1
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
             if not fused:
                 # the two-launch form: RoPE (q, k at position lens0 + t) and
                 # cache append, then the decode of the rotated q
-                r.rope_append(self.q[t], self.k[t], self.v[t], self.kc, self.vc, self.slots[t])
-                r.gqa_attn_decode(self.q[t][:, 0], self.kc, self.vc, self.lens[t], self.S_max, self.ws,
-                                  out=self.o)
+                r.rope_append(self.q[t], self.k[t], self.v[t], kc, vc, self.slots[t])
+                r.gqa_attn_decode(self.q[t][:, 0], kc, vc, self.lens[t], self.S_max, self.ws, out=self.o)
             else:
                 # one launch (plus the chunk merge): RoPE of q and k at
                 # position lens0 + t, append of k and v, attention
-                r.gqa_attn_decode_rope_append(self.q[t][:, 0], self.k[t][:, 0], self.v[t][:, 0], self.kc,
-                                              self.vc, self.lens[t], self.S_max, self.ws, out=self.o)
+                r.gqa_attn_decode_rope_append(self.q[t][:, 0], self.k[t][:, 0], self.v[t][:, 0], kc, vc,
+                                              self.lens[t], self.S_max, self.ws, out=self.o)
+            if events is not None:
+                e1.record()
+                events.append((e0, e1))
+
+
+def decode_length_sweep(rgc, iters=20, cache_sets=3, lengths=(256, 512, 1024, 2048, 4096, 8192)):
+    """Decode time against cache length at a fixed batch (64 sequences, all
+    of length L, 24 q / 8 KV heads, D 128, bf16), over rotated cache sets.
+    Cached decode reads each cached row once per step, so its time should be
+    linear in L (the O(N)-per-step cost of cached generation on page
+    "750美元从零训练3个LLM：一位开发者的实战复盘", section V3); a least-squares
+    line t = a + b L and its r^2 are reported."""
+    B, Hq, Hkv, D = 64, 24, 8, 128
+    S_max = max(lengths)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(404)
+    sets = []
+    for _ in range(cache_sets):
+        pair = []
+        for _ in range(2):
+            pair.append(torch.randn((B, Hkv, S_max, D), generator=gen, device="cuda").to(torch.bfloat16))
+        sets.append(tuple(pair))
+    q = torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    ws = rgc.decode_workspace(B, Hq, Hkv, D, S_max)
+    o = torch.empty_like(q)
+    rows = []
+    for L in lengths:
+        lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        run = lambda i: rgc.gqa_attn_decode(q, sets[i % cache_sets][0], sets[i % cache_sets][1], lens, L, ws, out=o)
+        for i in range(3):
+            run(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            run(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        byts = float(B) * L * Hkv * D * 2 * 2
+        rows.append({"L": L, "us_per_call": round(us, 3), "GB/s": round(byts / (us * 1e-6) / 1e9, 1)})
+    del sets
+    xs = [float(r["L"]) for r in rows]
+    ys = [r["us_per_call"] for r in rows]
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    sxy = sum((x - mx) * (y - my) for x, y in zip(xs, ys))
+    slope = sxy / sxx
+    icept = my - slope * mx
+    ss_res = sum((y - (icept + slope * x)) ** 2 for x, y in zip(xs, ys))
+    ss_tot = sum((y - my) ** 2 for y in ys)
+    return {"points": rows, "fit_us": {"intercept": round(icept, 3), "us_per_1k_tokens": round(slope * 1e3, 4),
+                                        "r2": round(1.0 - ss_res / ss_tot, 6)},
+            "cache_sets": cache_sets,
+            "workload": "64 sequences all of cache length L, 24q/8kv, D128, bf16, gqa_attn_decode (max_len = L)",
+            "pages": "cached generation costs O(N) per new token where recomputing costs O(N^2)"}
+
+
+def ceilings(iters=10):
+    """What this GPU delivers to a hand-written kernel: a streaming read of
+    2 GiB with 16-byte loads, and back-to-back bf16 MFMA (32x32x16) on four
+    accumulators per wave (ceilings/ceilings.hip)."""
+    import ctypes
+    path = os.path.join(ROOT, "ceilings", "libceil.so")
+    if not os.path.exists(path):
+        return {"error": "ceilings/libceil.so is not built"}
+    lib = ctypes.CDLL(path)
+    lib.ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                     ctypes.c_void_p]
+    lib.ceil_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    best_read = 0.0
+    read_rows = []
+    for wgs in (1024, 2048, 4096, 8192):
+        out = torch.empty(wgs * 256, dtype=torch.int32, device="cuda")
+        if lib.ceil_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()), wgs, stream):
+            return {"error": "ceil_stream_read refused"}
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            lib.ceil_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()), wgs, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        read_rows.append({"workgroups": wgs, "GB/s": round(gbs, 1)})
+        best_read = max(best_read, gbs)
+    del buf
+    mf_rows, best_mf = [], 0.0
+    for wgs, loop in ((512, 2048), (1024, 2048)):
+        out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+        lib.ceil_mfma_bf16(ctypes.c_void_p(out.data_ptr()), wgs, 64, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            lib.ceil_mfma_bf16(ctypes.c_void_p(out.data_ptr()), wgs, loop, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        flops = float(wgs) * 4 * loop * 4 * 32768 * iters
+        tf = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        mf_rows.append({"workgroups": wgs, "waves_per_simd": wgs * 4 // 1024, "TFLOP/s": round(tf, 1)})
+        best_mf = max(best_mf, tf)
+    return {"hbm_read_GBs": round(best_read, 1), "hbm_read_frac_of_spec": round(best_read / HBM_PEAK_GBS, 4),
+            "hbm_read_runs": read_rows,
+            "mfma_bf16_TFLOPs": round(best_mf, 1), "mfma_bf16_frac_of_spec": round(best_mf / BF16_PEAK_TFLOPS, 4),
+            "mfma_runs": mf_rows,
+            "kernels": "ceilings/ceilings.hip: grid-stride 16-byte reads of 2 GiB (4 loads in flight per lane); "
+                       "v_mfma_f32_32x32x16_bf16 back to back on 4 accumulators per wave, no memory traffic"}
 
 
 class Diff:
@@ -447,33 +653,127 @@ def time_prologues(pre, iters):
     return out
 
 
-def cpu_baseline(dec, seconds):
-    """Time the fp64 oracle's decode on the host: passes over the workload's
-    decode calls (lengths growing by one per call, as on the GPU) until about
-    ``seconds`` of CPU time have been spent."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(pre, dec, seconds):
+    """Time the fp64 oracle (as it stands) on the host cores, on bounded
+    samples of the two workloads of the step:
+      decode  passes over the ragged-decode calls (lengths growing by one per
+              call, as on the GPU) until about ``seconds`` have been spent;
+      prefill row blocks of 16 query rows at random slots of the 3.8B-shaped
+              batch (all 8 sequences and 24 heads), until about ``seconds``;
+    plus one-thread figures for the tiny fp32 workload (its whole prefill and
+    decode chain) and for sampled rows of the differential workload."""
     import oracle
+    from rope_gqa_causal_amd import synth
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     threads = int(os.environ.get("OMP_NUM_THREADS", threads))
+    # decode
     w = dec.w
     q = dec.q.cpu()
-    done_bytes, t_total, calls = 0.0, 0.0, 0
-    while calls == 0 or t_total < seconds:
+    done_bytes, t_dec, calls = 0.0, 0.0, 0
+    while calls == 0 or t_dec < seconds:
         t = calls % w.steps
         lens = dec.lens0_cpu + (t + 1)
         t0 = time.perf_counter()
         oracle.attn_decode(q[t][:, 0], dec.kc_cpu, dec.vc_cpu, lens, nthreads=threads)
-        t_total += time.perf_counter() - t0
+        t_dec += time.perf_counter() - t0
         done_bytes += dec.bytes_per_call[t]
         calls += 1
-    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} decode calls ({calls / w.steps:.1f} passes over the {w.steps} steps) of the "
-                      f"ragged-decode workload (64 sequences, all heads), fp64, {t_total:.1f} s"}
+    dec_gbs = done_bytes / t_dec / 1e9
+    # prefill: row blocks of the (rotated) q over the cache the bench filled
+    pw = pre.w
+    pq, pk, pv = pre.q.cpu(), pre.kc.cpu(), pre.vc.cpu()
+    g = torch.Generator().manual_seed(303)
+    flops, t_pre, blocks = 0.0, 0.0, 0
+    while blocks == 0 or t_pre < seconds:
+        s0 = int(torch.randint(0, pw.S - 16 + 1, (1,), generator=g))
+        qs = torch.full((pw.B,), s0, dtype=torch.int32)
+        t0 = time.perf_counter()
+        oracle.attn(pq[:, s0:s0 + 16], pk, pv, qs, nthreads=threads)
+        t_pre += time.perf_counter() - t0
+        flops += 4.0 * pw.D * pw.B * pw.Hq * sum(s0 + i + 1 for i in range(16))
+        blocks += 1
+    pre_gfs = flops / t_pre / 1e9
+    # one thread: the tiny fp32 workload's whole chain
+    tw = synth.WORKLOADS["tiny"]
+    T = tw.S + tw.steps
+    tq, tk, tv = synth.qkv(tw.B, T, tw.Hq, tw.Hkv, tw.D, synth.generator(tw.seed), tw.dtype)
+    tiny_flops = 4.0 * tw.D * tw.Hq * (sum(i + 1 for i in range(tw.S)) + sum(tw.S + i + 1 for i in range(tw.steps)))
+    n_tiny, t_tiny = 0, 0.0
+    while n_tiny == 0 or t_tiny < 1.0:
+        t0 = time.perf_counter()
+        qo, ko = tq.clone(), tk.clone()
+        oracle.rope_apply_(qo, None)
+        oracle.rope_apply_(ko, None)
+        kco = torch.zeros((tw.B, tw.Hkv, T, tw.D), dtype=tw.dtype)
+        vco = torch.zeros_like(kco)
+        oracle.kv_cache_append_(kco, vco, ko, tv, torch.zeros(tw.B, dtype=torch.int32))
+        oracle.attn(qo[:, :tw.S], kco, vco, nthreads=1)
+        for i in range(tw.steps):
+            oracle.attn_decode(qo[:, tw.S + i], kco, vco, torch.full((tw.B,), tw.S + i + 1, dtype=torch.int32),
+                               nthreads=1)
+        t_tiny += time.perf_counter() - t0
+        n_tiny += 1
+    # one thread: sampled rows of the differential workload
+    dw = synth.WORKLOADS["diff"]
+    dg = synth.generator(dw.seed)
+    q1 = synth.normal((dw.B, dw.S, dw.Hq, dw.D), dg)
+    q2 = synth.normal((dw.B, dw.S, dw.Hq, dw.D), dg)
+    k1, k2, dv = (synth.normal((dw.B, dw.Hkv, dw.S, dw.D), dg) for _ in range(3))
+    dflops, t_diff, dblocks = 0.0, 0.0, 0
+    while dblocks == 0 or t_diff < 2.0:
+        s0 = int(torch.randint(0, dw.S - 4 + 1, (1,), generator=g))
+        qs = torch.full((dw.B,), s0, dtype=torch.int32)
+        t0 = time.perf_counter()
+        oracle.diff_attn(q1[:, s0:s0 + 4], q2[:, s0:s0 + 4], k1, k2, dv, dw.lam, qs, nthreads=1)
+        t_diff += time.perf_counter() - t0
+        dflops += 2 * 4.0 * dw.D * dw.B * dw.Hq * sum(s0 + i + 1 for i in range(4))
+        dblocks += 1
+    return {"value": round(dec_gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"decode: {calls} calls ({calls / w.steps:.1f} passes over the {w.steps} steps) of the "
+                      f"ragged-decode workload (64 sequences, all heads), fp64, {t_dec:.1f} s",
+            "prefill": {"value": round(pre_gfs, 3), "unit": "GFLOP/s", "cores": threads,
+                        "sample": f"{blocks} blocks of 16 query rows at random slots of the 8 x 2048, 24q/8kv, "
+                                  f"D128 batch (all sequences and heads), fp64, {t_pre:.1f} s"},
+            "one_thread": {
+                "tiny": {"us_per_run": round(t_tiny / n_tiny * 1e6, 1),
+                         "GFLOP/s": round(tiny_flops * n_tiny / t_tiny / 1e9, 4),
+                         "sample": f"{n_tiny} runs of the tiny fp32 chain (RoPE, append, 16-row prefill, 8 decode "
+                                   "steps; 4q/2kv, D32)"},
+                "diff": {"GFLOP/s": round(dflops / t_diff / 1e9, 4),
+                         "sample": f"{dblocks} blocks of 4 query rows at random slots of the differential workload "
+                                   f"(B4 x 1024, 16q/8kv, two maps of D64), {t_diff:.1f} s"}},
+            "note": "fp64 CPU oracle as it stands: a baseline, not a target"}
+
+
+PAGES_CONTEXT = {
+    "cached_generation": "278 s -> 28 s for 100 new tokens after a 512-token prompt, whole model, hardware "
+                         "not stated (page '750美元从零训练3个LLM：一位开发者的实战复盘', section V3)",
+    "training_throughput": "about 480,000 tokens/s in steady state on 8x B200 (DDP, bf16 with FP8 GEMMs), "
+                           "whole-model training of the 24q/8kv 3.8B model at 1024 context (page "
+                           "'训练3.8B LLM至0.384 CORE，成本998美元 – Hugo Vergnes', sections 结果 and 提高吞吐量)",
+    "note": "context only: whole-model figures on other hardware, not comparable with these kernel rates",
+}
 
 
 def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
@@ -485,9 +785,11 @@ def main():
     import rope_gqa_causal_amd as rgc
     from rope_gqa_causal_amd import synth
 
+    do_pre = args.phase in ("all", "prefill")
+    do_dec = args.phase in ("all", "decode")
     print("[bench] setting up inputs", file=sys.stderr, flush=True)
-    pre = Prefill(rgc, synth)
-    dec = Decode(rgc, synth)
+    pre = Prefill(rgc, synth) if do_pre else None
+    dec = Decode(rgc, synth, args.cache_sets) if do_dec else None
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
         dst = torch.empty_like(src)
@@ -496,67 +798,41 @@ def main():
         del src, dst
 
     for i in range(args.warmup):
-        pre.run(False)
-        dec.run(fused=True)
+        if do_pre:
+            pre.run(False)
+        if do_dec:
+            dec.run()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     phase = []
+    call_events = []
     torch.cuda.synchronize()
     t_start.record()
-    rgc.timing_report()  # clear
     for i in range(args.steps):
         a = torch.cuda.Event(enable_timing=True)
         m = torch.cuda.Event(enable_timing=True)
         z = torch.cuda.Event(enable_timing=True)
         a.record()
-        pre.run(True)
+        if do_pre:
+            pre.run(True)
         m.record()
-        # Events between the decode kernels break their back-to-back issue
-        # (a few us per call), so only the last timed step carries them: the
-        # library brackets each kernel it launches there, and the decode
-        # roofline averages that step's 32 launches.
-        last = i == args.steps - 1
-        if last:
-            rgc.timing_enable(True)
-        dec.run(fused=True)
-        if last:
-            rgc.timing_enable(False)
+        # Events between the decode calls break their back-to-back issue (a
+        # few us per call), so only the last timed step carries them.
+        if do_dec:
+            dec.run(events=call_events if i == args.steps - 1 else None)
         z.record()
         phase.append((a, m, z))
     t_end.record()
     torch.cuda.synchronize()
-    ktimes = rgc.timing_report()
     print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
 
     total_ms = t_start.elapsed_time(t_end)
-    pre_ms = sum(a.elapsed_time(m) for a, m, _ in phase)
-    dec_ms = sum(m.elapsed_time(z) for _, m, z in phase)
-    dec_bytes = sum(dec.bytes_per_call) * args.steps
-    value = dec_bytes / (dec_ms * 1e-3) / 1e9
-    prefill_tflops = pre.flops * args.steps / (pre_ms * 1e-3) / 1e12
-
-    # Per-launch kernel durations: the prefill from HIP events around each
-    # call (one kernel per call), the decode kernels from the library's own
-    # per-kernel events in the last timed step.
-    pk_ms = [e0.elapsed_time(e1) for e0, e1 in pre.events]
-    pk_avg = sum(pk_ms) / len(pk_ms)
-    n_split, split_us = ktimes["decode_split_kernel"]
-    n_comb, comb_us = ktimes.get("decode_combine_kernel", (n_split, 0.0))
-    if n_split != dec.w.steps or n_comb != dec.w.steps:
-        raise SystemExit(f"expected {dec.w.steps} decode launches per kernel, got {ktimes}")
-    dk_avg = split_us / n_split * 1e-3               # ms
-    op_avg = dk_avg + comb_us / n_comb * 1e-3        # ms, kernel time of split + merge
-    dk_bytes_avg = sum(dec.bytes_per_call) / len(dec.bytes_per_call)
-    dec_achieved = dk_bytes_avg / (dk_avg * 1e-3) / 1e9
-    op_achieved = dk_bytes_avg / (op_avg * 1e-3) / 1e9
-    pre_achieved = pre.flops / (pk_avg * 1e-3) / 1e12
-
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -570,36 +846,73 @@ def main():
         "config": {
             "workload": "prefill 3.8B-shaped (B8 x 2048, 24q/8kv, D128) + ragged decode "
                         "(64 seqs, L~U{256..2048}, 24q/8kv, D128, 32 steps); bf16, fp32 accumulate",
-            "global_batch": dec.w.B,
-            "seq_len": pre.w.S,
+            "global_batch": synth.WORKLOADS["ragged_decode"].B,
+            "seq_len": synth.WORKLOADS["prefill3p8b"].S,
             "parallelism": "single GPU",
+            "cache_sets": args.cache_sets if do_dec else None,
+            "phase": args.phase,
         },
-        "prefill": {
-            "tflops": round(prefill_tflops, 2),
-            "phase_ms_per_step": round(pre_ms / args.steps, 4),
-            "note": "fused RoPE q,k + append, then causal prefill; FLOPs count unmasked pairs x 4D",
-        },
-        "decode_phase_ms_per_step": round(dec_ms / args.steps, 4),
-        "roofline": {
+    }
+    if do_dec:
+        dec_ms = sum(m.elapsed_time(z) for _, m, z in phase)
+        dec_bytes = sum(dec.bytes_per_call) * args.steps
+        result["value"] = round(dec_bytes / (dec_ms * 1e-3) / 1e9, 2)
+        result["decode_phase_ms_per_step"] = round(dec_ms / args.steps, 4)
+        # The whole decode op per call (split + merge kernels, and the gap
+        # between them), from the events around each call of the last step.
+        op_ms = [e0.elapsed_time(e1) for e0, e1 in call_events]
+        op_avg = sum(op_ms) / len(op_ms)
+        bytes_avg = sum(dec.bytes_per_call) / len(dec.bytes_per_call)
+        op_achieved = bytes_avg / (op_avg * 1e-3) / 1e9
+        # The split kernel alone: the instrumented build times each kernel
+        # of one more (untimed) decode phase.
+        rgc.timing_report()  # clear
+        with rgc.kernel_timing():
+            dec.run()
+        torch.cuda.synchronize()
+        kt = rgc.timing_report()
+        n_split, split_us = kt["decode_split_kernel"]
+        n_comb, comb_us = kt.get("decode_combine_kernel", (n_split, 0.0))
+        if n_split != dec.w.steps or n_comb != dec.w.steps:
+            raise SystemExit(f"expected {dec.w.steps} decode launches per kernel, got {kt}")
+        split_avg = split_us / n_split * 1e-3
+        split_achieved = bytes_avg / (split_avg * 1e-3) / 1e9
+        result["roofline"] = {
             "bound": "hbm",
-            "kernel": "decode_split_kernel with the token's RoPE and append inside (the decode's dominant "
-                      "kernel: streams the cache)",
-            "achieved": round(dec_achieved, 2),
+            "kernel": "gqa_attn_decode_rope_append: decode_split_kernel (with the token's RoPE and append "
+                      "inside) + decode_combine_kernel, per call",
+            "achieved": round(op_achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(dec_achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic("decode", "decode.hip", dk_bytes_avg),
-            "algorithmic_bytes_per_launch": round(dk_bytes_avg),
-            "avg_launch_us": round(dk_avg * 1e3, 3),
-            "op": {
-                "kernels": "decode_split_kernel + decode_combine_kernel (gqa_attn_decode_rope_append)",
-                "avg_kernel_us": round(op_avg * 1e3, 3),
-                "achieved": round(op_achieved, 2),
-                "frac": round(op_achieved / HBM_PEAK_GBS, 4),
-                "traffic": stored_traffic("decode_op", "decode.hip", dk_bytes_avg),
+            "frac": round(op_achieved / HBM_PEAK_GBS, 4),
+            "traffic": stored_traffic("decode_op", "decode.hip", bytes_avg),
+            "algorithmic_bytes_per_launch": round(bytes_avg),
+            "avg_launch_us": round(op_avg * 1e3, 3),
+            "timing": "HIP events around each of the 32 decode calls of the last timed step, on the stream the "
+                      "library launches on",
+            "cache_sets": args.cache_sets,
+            "split_kernel": {
+                "kernel": "decode_split_kernel (streams the cache; carries all the algorithmic bytes)",
+                "avg_launch_us": round(split_avg * 1e3, 3),
+                "achieved": round(split_achieved, 2),
+                "frac": round(split_achieved / HBM_PEAK_GBS, 4),
+                "merge_avg_us": round(comb_us / n_comb, 3),
+                "traffic": stored_traffic("decode", "decode.hip", bytes_avg),
+                "timing": "instrumented build (librgc_timed.so): HIP events around each kernel, one extra "
+                          "untimed decode phase on the same rotated cache sets",
             },
-        },
-        "roofline_prefill": {
+        }
+    if do_pre:
+        pre_ms = sum(a.elapsed_time(m) for a, m, _ in phase)
+        pk_ms = [e0.elapsed_time(e1) for e0, e1 in pre.events]
+        pk_avg = sum(pk_ms) / len(pk_ms)
+        pre_achieved = pre.flops / (pk_avg * 1e-3) / 1e12
+        result["prefill"] = {
+            "tflops": round(pre.flops * args.steps / (pre_ms * 1e-3) / 1e12, 2),
+            "phase_ms_per_step": round(pre_ms / args.steps, 4),
+            "note": "fused RoPE q,k + append, then causal prefill; FLOPs count unmasked pairs x 4D",
+        }
+        result["roofline_prefill"] = {
             "bound": "mfma",
             "kernel": "gqa_attn_prefill",
             "achieved": round(pre_achieved, 2),
@@ -609,19 +922,28 @@ def main():
             "traffic": stored_traffic("prefill", "prefill.hip", None),
             "algorithmic_flops_per_launch": pre.flops,
             "avg_launch_us": round(pk_avg * 1e3, 3),
-        },
-    }
-    if not args.no_extras:
+            "mfma_util": stored_mfma_util(),
+        }
+        if result["value"] is None:
+            result["value"] = round(pre_achieved, 2)
+            result["unit"] = "TFLOP/s"
+    if not args.no_extras and args.phase == "all":
         result["diff_attn"] = Diff(rgc, synth).time(max(args.steps, 5))
         result["prologue"] = time_prologues(pre, max(args.steps, 5))
         result["varlen_prefill"] = Varlen(rgc, synth).time(max(args.steps, 5))
         result["backward"] = time_backward(rgc, synth, max(args.steps, 3))
         result["generation_125m"] = Generation(rgc, synth).time()
         print("[bench] timed the variant lines", file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
+        result["decode_length_sweep"] = decode_length_sweep(rgc, cache_sets=max(args.cache_sets, 1))
+        result["ceilings"] = ceilings()
+        print("[bench] timed the length sweep and the ceilings", file=sys.stderr, flush=True)
+    elif args.with_ceilings:
+        result["ceilings"] = ceilings(iters=2)
+    result["pages_context"] = PAGES_CONTEXT
+    if not args.no_cpu_baseline and args.phase == "all":
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+        result["cpu_baseline"] = cpu_baseline(pre, dec, args.cpu_seconds)
+    print(json.dumps(result, ensure_ascii=False), flush=True)
 
 
 if __name__ == "__main__":

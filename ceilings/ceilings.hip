@@ -1,0 +1,81 @@
+// ceilings.hip -- two measurement kernels that set what this MI355X delivers
+// to a hand-written kernel, beside the published peaks: a streaming read of
+// device memory and a loop of bf16 matrix-core instructions.  Measurement
+// only; the attention library does not use them.
+//
+//  * ceil_stream_read: a fixed grid of workgroups strides over the buffer
+//    with 16-byte loads, four in flight per lane, and folds what it reads
+//    into one word per thread (written out, so no load can be dropped).
+//    bytes / time is the read bandwidth a streaming kernel can reach.
+//  * ceil_mfma_bf16: every wave issues back-to-back
+//    v_mfma_f32_32x32x16_bf16 on four independent accumulators (no memory
+//    traffic in the loop).  flops / time is the matrix-core rate a kernel
+//    can reach at the clock the chip holds under that load.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                          uint32_t* __restrict__ out) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
+    acc ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = src[i];
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+__global__ void __launch_bounds__(256) mfma_bf16_kernel(float* __restrict__ out, int iters) {
+  const uint32_t t = threadIdx.x;
+  u32x4 av = {0x3F803F80u ^ t, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  u32x4 bv = {0x3C003C00u, 0x3C003C00u ^ t, 0x3C003C00u, 0x3C003C00u};
+  const bf16x8 a = __builtin_bit_cast(bf16x8, av), b = __builtin_bit_cast(bf16x8, bv);
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16) from src with `wgs` workgroups of 256
+// threads; out receives wgs * 256 words.  0, or -1 for a bad argument, or
+// -9 when the launch is refused.
+int ceil_stream_read(const void* src, size_t bytes, uint32_t* out, int wgs, void* stream) {
+  if (!src || !out || wgs <= 0 || bytes % 16 != 0) return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4*)src, bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -9;
+}
+
+// `wgs` workgroups of 4 waves, each wave `iters` x 4 matrix instructions of
+// 32 x 32 x 16 (32768 flops each); out receives wgs * 256 floats.
+int ceil_mfma_bf16(float* out, int wgs, int iters, void* stream) {
+  if (!out || wgs <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(mfma_bf16_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : -9;
+}
+
+}  // extern "C"

@@ -22,9 +22,9 @@
  * Conventions shared by every entry point:
  *  - Every data pointer is a DEVICE pointer (HIP global memory) unless the
  *    argument says "host".  The caller owns every buffer; the library never
- *    allocates, frees or synchronises and keeps no mutable global state,
- *    except for the opt-in per-kernel timing (rgc_timing_enable /
- *    rgc_timing_report), which creates HIP events and waits for them.
+ *    allocates, frees or synchronises and keeps no mutable global state
+ *    (per-kernel timing lives in a separate instrumented build,
+ *    rgc_timing.h).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns.
  *  - Shapes are element counts; strides are in ELEMENTS, not bytes.  The
@@ -88,25 +88,6 @@ int rgc_abi_version(void);
 
 /* Static English text for a status code; never NULL. */
 const char* rgc_status_string(int status);
-
-/*
- * Per-kernel timing, for measurement.  While on, every kernel the library
- * launches is bracketed by two HIP events recorded on the stream it runs
- * on, so each kernel's own duration is taken on the device clock apart from
- * the other kernels of the same call (each event pair costs a few
- * microseconds of stream time, so leave it off outside measurement).
- *   rgc_timing_enable   on != 0 starts recording, 0 stops (what was
- *                       recorded stays until the next report).  RGC_OK.
- *   rgc_timing_report   waits for the recorded events, writes one line
- *                       "kernel_name launches total_microseconds\n" per
- *                       kernel into buf (NUL-terminated) and clears the
- *                       record.  Returns the bytes written without the NUL,
- *                       or RGC_ERR_ARG when buf is NULL or too small or an
- *                       event could not be read (the record is cleared in
- *                       every case).  Host-thread safe.
- */
-int rgc_timing_enable(int on);
-long rgc_timing_report(char* buf, size_t buf_bytes);
 
 /*
  * rgc_rope_apply -- rotary position embedding, in place.

@@ -15,6 +15,7 @@ the library is missing or no GPU is present, every call raises.
     o = rgc.gqa_attn_decode(q1, kc, vc, lens, max_len, ws)
     o = rgc.diff_attn_prefill(q1, q2, k1c, k2c, vc, 0.8, q_start)
 """
+import contextlib
 import ctypes
 import os
 
@@ -24,12 +25,14 @@ __all__ = [
     "RgcError", "library", "rope_apply", "kv_cache_append", "rope_append", "norm_rope_append",
     "gqa_attn_prefill",
     "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace", "diff_attn_prefill",
+    "gqa_attn_decode_rope_append",
     "gqa_attn_prefill_varlen", "rope_backward", "gqa_attn_backward", "backward_workspace",
-    "ROPE_HALF", "ROPE_INTERLEAVED", "timing_enable", "timing_report",
+    "ROPE_HALF", "ROPE_INTERLEAVED", "timed_library", "kernel_timing", "timing_report",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librgc.so")
+TIMED_LIB_PATH = os.path.join(_HERE, "librgc_timed.so")
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 _F32, _BF16 = 0, 1
 
@@ -43,8 +46,6 @@ _sz = ctypes.c_size_t
 _SIGNATURES = {
     "rgc_abi_version": (_i, []),
     "rgc_status_string": (ctypes.c_char_p, [_i]),
-    "rgc_timing_enable": (_i, [_i]),
-    "rgc_timing_report": (ctypes.c_long, [ctypes.c_char_p, _sz]),
     "rgc_rope_apply": (_i, [_p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _d, _i, _p]),
     "rgc_rope_backward": (_i, [_p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _d, _i, _p]),
     "rgc_gqa_attn_backward_workspace_size": (_sz, [_i, _i, _i]),
@@ -73,7 +74,14 @@ _SIGNATURES = {
                                              _p, _i, _d, _i, _f, _p, _sz, _p, _p, _p]),
 }
 
+_TIMING_SIGNATURES = {
+    "rgc_timing_enable": (_i, [_i]),
+    "rgc_timing_report": (ctypes.c_long, [ctypes.c_char_p, _sz]),
+}
+
 _lib = None
+_timed_lib = None
+_active = None  # the library calls go to: the product one, or the timed one inside kernel_timing()
 
 
 class RgcError(RuntimeError):
@@ -84,25 +92,38 @@ class RgcError(RuntimeError):
         self.status = status
 
 
+def _load(path, signatures):
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m rope_gqa_causal_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in signatures.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
 def library():
     """Load ``librgc.so`` (built by ``rope_gqa_causal_amd.build``); raise if absent."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with `python -m rope_gqa_causal_amd.build` "
-                "(there is no CPU fallback)")
-        lib = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = lib
+        _lib = _load(LIB_PATH, _SIGNATURES)
     return _lib
 
 
+def timed_library():
+    """Load the instrumented build ``librgc_timed.so`` (same kernels, plus
+    per-kernel timing); raise if absent.  For measurement only."""
+    global _timed_lib
+    if _timed_lib is None:
+        _timed_lib = _load(TIMED_LIB_PATH, {**_SIGNATURES, **_TIMING_SIGNATURES})
+    return _timed_lib
+
+
 def _call(name, *args):
-    lib = library()
+    lib = _active if _active is not None else library()
     st = getattr(lib, name)(*args)
     if st != 0:
         raise RgcError(name, st, lib.rgc_status_string(st).decode())
@@ -138,19 +159,32 @@ def _lens(t, B, name):
     return t
 
 
-def timing_enable(on=True):
-    """Start (or stop) per-kernel timing: each kernel the library launches is
-    bracketed by HIP events on its own stream until switched off."""
-    _call("rgc_timing_enable", 1 if on else 0)
+@contextlib.contextmanager
+def kernel_timing():
+    """Route the calls made inside the block through the instrumented build
+    with per-kernel timing on: each kernel it launches is bracketed by HIP
+    events on its own stream.  Read the result with ``timing_report()``."""
+    global _active
+    lib = timed_library()
+    prev = _active
+    _active = lib
+    lib.rgc_timing_enable(1)
+    try:
+        yield
+    finally:
+        lib.rgc_timing_enable(0)
+        _active = prev
 
 
 def timing_report():
-    """Per-kernel {name: (launches, total microseconds)} recorded since the
-    last report (waits for the events; clears the record)."""
+    """Per-kernel {name: (launches, total microseconds)} recorded by the
+    instrumented build since the last report (waits for the events; clears
+    the record)."""
+    lib = timed_library()
     buf = ctypes.create_string_buffer(1 << 16)
-    n = library().rgc_timing_report(buf, len(buf))
+    n = lib.rgc_timing_report(buf, len(buf))
     if n < 0:
-        raise RgcError("rgc_timing_report", n, library().rgc_status_string(n).decode())
+        raise RgcError("rgc_timing_report", n, lib.rgc_status_string(n).decode())
     out = {}
     for line in buf.value.decode().splitlines():
         name, calls, us = line.split()
@@ -341,12 +375,8 @@ def decode_workspace(B, Hq, Hkv, D, max_len, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def gqa_attn_decode_rope_append(q, k_new, v_new, k_cache, v_cache, seq_lens, max_len=None, workspace=None,
-                                base=10000.0, style=ROPE_HALF, scale=None, out=None, lse=None, err_flag=None):
-    """One generation step in one decode launch: q [B,Hq,D] and k_new [B,Hkv,D] turned at
-    position seq_lens[b]-1, k_new (rotated) and v_new [B,Hkv,D] written to that cache slot,
-    and the attention of q over slots 0..seq_lens[b]-1.  q is left unrotated; bf16 only."""
-    _gpu(q, k_new, v_new, k_cache, v_cache, seq_lens, workspace, out, lse, err_flag)
+def _decode_rope_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, max_len, out, lse, err_flag):
+    _gpu(q, k_new, v_new, k_cache, v_cache, seq_lens, out, lse, err_flag)
     B, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
     if v_cache.stride() != k_cache.stride():
@@ -355,21 +385,34 @@ def gqa_attn_decode_rope_append(q, k_new, v_new, k_cache, v_cache, seq_lens, max
         raise ValueError("k_new and v_new must be [B,Hkv,D] with one set of strides")
     if k_new.stride(2) != 1 or q.stride(2) != 1:
         raise ValueError("q, k_new and v_new need unit stride along D")
-    if scale is None:
-        scale = D ** -0.5
     if max_len is None:
         max_len = S_max
-    if workspace is None:
-        workspace = decode_workspace(B, Hq, Hkv, D, max_len, q.device)
     o = torch.empty_like(q) if out is None else out
     seq_lens = _lens(seq_lens, B, "seq_lens")
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (B, Hq)):
         raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
-    _call("rgc_gqa_attn_decode_rope_append", _ptr(o), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
-          _ptr(v_cache), _dtype(q), B, Hq, Hkv, D, S_max, q.stride(0), q.stride(1), k_new.stride(0),
-          k_new.stride(1), o.stride(0), o.stride(1), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
-          _ptr(seq_lens), int(max_len), float(base), int(style), float(scale), _ptr(workspace),
+    args = (_ptr(o), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _dtype(q), B, Hq, Hkv, D,
+            S_max, q.stride(0), q.stride(1), k_new.stride(0), k_new.stride(1), o.stride(0), o.stride(1),
+            k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), _ptr(seq_lens), int(max_len))
+    return o, args, max_len
+
+
+def gqa_attn_decode_rope_append(q, k_new, v_new, k_cache, v_cache, seq_lens, max_len=None, workspace=None,
+                                base=10000.0, style=ROPE_HALF, scale=None, out=None, lse=None, err_flag=None):
+    """One generation step in one decode launch: q [B,Hq,D] and k_new [B,Hkv,D] turned at
+    position seq_lens[b]-1, k_new (rotated) and v_new [B,Hkv,D] written to that cache slot,
+    and the attention of q over slots 0..seq_lens[b]-1.  q is left unrotated; bf16 only."""
+    _gpu(workspace)
+    o, args, max_len = _decode_rope_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, max_len, out, lse,
+                                                err_flag)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if scale is None:
+        scale = D ** -0.5
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, Hkv, D, max_len, q.device)
+    _call("rgc_gqa_attn_decode_rope_append", *args, float(base), int(style), float(scale), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(lse), _ptr(err_flag), _stream(q))
     return o
 

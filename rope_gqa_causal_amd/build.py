@@ -1,8 +1,13 @@
-"""Build the gfx950 HIP library ``librgc.so`` in-tree.
+"""Build the gfx950 HIP libraries in-tree.
 
 Each ``csrc/*.hip`` is compiled for gfx950 only (``--offload-arch=gfx950``)
-and the objects are linked into ``rope_gqa_causal_amd/librgc.so``.  Packed
-fp32 VALU instructions are disabled for the device code.
+and the objects are linked into ``rope_gqa_causal_amd/librgc.so``, the
+product library.  The same sources are compiled a second time with
+``-DRGC_KERNEL_TIMING`` into ``librgc_timed.so``, an instrumented build for
+measurement only: it also exports the per-kernel timing calls of
+``include/rgc_timing.h`` (HIP events around every kernel it launches), and
+it is the only build that keeps any global state.  Packed fp32 VALU
+instructions are disabled for the device code.
 """
 import os
 import subprocess
@@ -13,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librgc.so")
+TIMED_LIB = os.path.join(HERE, "librgc_timed.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -40,9 +46,11 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src, verbose):
-    obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
+def _compile(src, timed, verbose):
+    obj_dir = os.path.join(OBJ_DIR, "timed") if timed else OBJ_DIR
+    obj = os.path.join(obj_dir, os.path.basename(src)[:-4] + ".o")
+    extra = ["-DRGC_KERNEL_TIMING=1"] if timed else []
+    cmd = [HIPCC] + FLAGS + extra + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,17 +63,23 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(os.path.join(OBJ_DIR, "timed"), exist_ok=True)
+    srcs = sources()
+    jobs = [(s, False) for s in srcs] + [(s, True) for s in srcs]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], j[1], verbose), jobs))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], TIMED_LIB, verbose)
     return LIB
 
 

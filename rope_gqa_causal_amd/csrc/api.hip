@@ -475,13 +475,15 @@ int rgc_gqa_attn_decode(void* o, const void* q, const void* k_cache, const void*
   return hip_status(launch_decode_bf16(p, workspace, s));
 }
 
-int rgc_gqa_attn_decode_rope_append(void* o, const void* q, const void* k_new, const void* v_new, void* k_cache,
-                                    void* v_cache, int dtype, int B, int Hq, int Hkv, int D, int S_max,
-                                    int64_t q_sb, int64_t q_sh, int64_t n_sb, int64_t n_sh, int64_t o_sb,
-                                    int64_t o_sh, int64_t kv_sb, int64_t kv_sh, int64_t kv_ss,
-                                    const int32_t* seq_lens, int max_len, double base, int style, float scale,
-                                    void* workspace, size_t ws_bytes, float* lse, int32_t* err_flag,
-                                    void* stream) {
+namespace {
+
+// The one-launch step.
+int decode_rope_append_impl(void* o, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                            void* v_cache, int dtype, int B, int Hq, int Hkv, int D, int S_max, int64_t q_sb,
+                            int64_t q_sh, int64_t n_sb, int64_t n_sh, int64_t o_sb, int64_t o_sh, int64_t kv_sb,
+                            int64_t kv_sh, int64_t kv_ss, const int32_t* seq_lens, int max_len, double base,
+                            int style, float scale, void* workspace, size_t ws_bytes, float* lse,
+                            int32_t* err_flag, void* stream) {
   int st = check_attn_common(dtype, B, 1, Hq, Hkv, D, S_max);
   if (st != RGC_OK) return st;
   if (dtype != RGC_BF16) return RGC_ERR_DTYPE;
@@ -536,11 +538,18 @@ int rgc_gqa_attn_decode_rope_append(void* o, const void* q, const void* k_new, c
   return hip_status(launch_decode_rope_bf16(p, r, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int rgc_timing_enable(int on) { return timing_enable(on); }
+}  // namespace
 
-long rgc_timing_report(char* buf, size_t buf_bytes) {
-  const long n = timing_report(buf, buf_bytes);
-  return n < 0 ? (long)RGC_ERR_ARG : n;
+int rgc_gqa_attn_decode_rope_append(void* o, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                    void* v_cache, int dtype, int B, int Hq, int Hkv, int D, int S_max,
+                                    int64_t q_sb, int64_t q_sh, int64_t n_sb, int64_t n_sh, int64_t o_sb,
+                                    int64_t o_sh, int64_t kv_sb, int64_t kv_sh, int64_t kv_ss,
+                                    const int32_t* seq_lens, int max_len, double base, int style, float scale,
+                                    void* workspace, size_t ws_bytes, float* lse, int32_t* err_flag,
+                                    void* stream) {
+  return decode_rope_append_impl(o, q, k_new, v_new, k_cache, v_cache, dtype, B, Hq, Hkv, D, S_max, q_sb, q_sh,
+                                 n_sb, n_sh, o_sb, o_sh, kv_sb, kv_sh, kv_ss, seq_lens, max_len, base, style,
+                                 scale, workspace, ws_bytes, lse, err_flag, stream);
 }
 
 }  // extern "C"

@@ -10,8 +10,10 @@
 namespace rgc {
 
 // Brackets one kernel launch with HIP events on its stream while per-kernel
-// timing is on (timing.hip); does nothing otherwise.  Construct it right
-// before the launch, in the scope that ends right after it.
+// timing is on.  Only the instrumented build (RGC_KERNEL_TIMING, timing.hip)
+// records anything; in the product build it is an empty object.  Construct
+// it right before the launch, in the scope that ends right after it.
+#ifdef RGC_KERNEL_TIMING
 class KernelTimer {
  public:
   KernelTimer(const char* name, hipStream_t stream);
@@ -26,6 +28,14 @@ class KernelTimer {
 };
 int timing_enable(int on);
 long timing_report(char* buf, size_t bytes);
+#else
+class KernelTimer {
+ public:
+  KernelTimer(const char*, hipStream_t) {}
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+};
+#endif
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 enum { ROPE_HALF = 0, ROPE_INTERLEAVED = 1 };
@@ -145,5 +155,6 @@ struct DecodeRope {
   double theta[64];    // base^(-2i/D) for i < D/2, formed on the host in fp64
 };
 hipError_t launch_decode_rope_bf16(const AttnParams& p, const DecodeRope& r, void* ws, hipStream_t stream);
+
 
 }  // namespace rgc

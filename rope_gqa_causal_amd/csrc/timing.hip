@@ -1,4 +1,6 @@
-// timing.hip -- per-kernel launch timing for measurement (host code only).
+// timing.hip -- per-kernel launch timing for measurement (host code only),
+// compiled into the instrumented build (RGC_KERNEL_TIMING) only: the product
+// library keeps no global state.
 //
 // While timing is on, every kernel the library launches is bracketed by two
 // HIP events recorded on the stream it is launched on, so each kernel's own
@@ -18,6 +20,9 @@
 #include <vector>
 
 #include "launch.h"
+
+#ifdef RGC_KERNEL_TIMING
+#include "../../include/rgc_timing.h"
 
 namespace rgc {
 namespace {
@@ -109,3 +114,16 @@ long timing_report(char* buf, size_t bytes) {
 }
 
 }  // namespace rgc
+
+extern "C" {
+
+int rgc_timing_enable(int on) { return rgc::timing_enable(on); }
+
+long rgc_timing_report(char* buf, size_t buf_bytes) {
+  const long n = rgc::timing_report(buf, buf_bytes);
+  return n < 0 ? -10L /* RGC_ERR_ARG */ : n;
+}
+
+}  // extern "C"
+
+#endif  // RGC_KERNEL_TIMING

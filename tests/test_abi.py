@@ -237,8 +237,18 @@ def test_binding_refuses_cpu_tensors():
         rgc.rope_apply(x)
 
 
-def test_timing_switch_and_empty_report():
+def test_product_library_has_no_timing_state_and_the_timed_build_exports_all():
     lib = rgc.library()
+    assert not hasattr(lib, "rgc_timing_enable") and not hasattr(lib, "rgc_timing_report")
+    timed = rgc.timed_library()
+    timing_names = sorted(set(re.findall(r"\b(rgc_[a-z0-9_]+)\s*\(", open(os.path.join(ROOT, "include", "rgc_timing.h")).read())))
+    assert timing_names == ["rgc_timing_enable", "rgc_timing_report"]
+    for n in _declared() + timing_names:
+        assert hasattr(timed, n), n
+
+
+def test_timing_switch_and_empty_report():
+    lib = rgc.timed_library()
     assert lib.rgc_timing_enable(1) == OK
     assert lib.rgc_timing_enable(0) == OK
     assert rgc.timing_report() == {}  # nothing launched: no lines

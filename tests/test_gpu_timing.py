@@ -1,5 +1,5 @@
-"""GPU: the library's per-kernel timing records each kernel of a call apart,
-and only while switched on.  Also shows which decode form a shape takes: a
+"""GPU: the instrumented build's per-kernel timing records each kernel of a
+call apart, and only while switched on.  Also shows which decode form a shape takes: a
 small grid walks each sequence in one workgroup (one kernel), a large one
 splits the cache (split kernel, then the merge)."""
 import pytest
@@ -26,14 +26,13 @@ def _decode_setup(B, Hq, Hkv, D, S_max, seed):
 def test_decode_kernels_are_timed_apart_and_only_while_on(B, Hq, Hkv, S_max, kernels):
     q, kc, vc, lens, ws = _decode_setup(B, Hq, Hkv, 128, S_max, 21)
     rgc.timing_report()  # clear
-    rgc.gqa_attn_decode(q, kc, vc, lens, S_max, ws)  # timing off: not recorded
-    rgc.timing_enable(True)
-    try:
+    ref = rgc.gqa_attn_decode(q, kc, vc, lens, S_max, ws)  # product build: not recorded
+    with rgc.kernel_timing():
         for _ in range(3):
-            rgc.gqa_attn_decode(q, kc, vc, lens, S_max, ws)
-    finally:
-        rgc.timing_enable(False)
+            o = rgc.gqa_attn_decode(q, kc, vc, lens, S_max, ws)
     rgc.gqa_attn_decode(q, kc, vc, lens, S_max, ws)  # off again
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)  # the instrumented build runs the same kernels
     rep = rgc.timing_report()
     assert set(rep) == kernels, rep
     for name, (calls, us) in rep.items():
