@@ -371,6 +371,33 @@ int rgc_gqa_attn_decode_rope_append(void* o, const void* q, const void* k_new,
                                     void* workspace, size_t ws_bytes, float* lse,
                                     int32_t* err_flag, void* stream);
 
+/*
+ * rgc_gqa_attn_decode_rope_append_static -- rgc_gqa_attn_decode_rope_append
+ * without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The chunk partials go to a device array the library
+ * owns, 16 MiB per GPU (each GPU the library runs on holds its copy until
+ * the process ends); its address is looked up once per device, on the first
+ * call made with that device current.  Nothing is allocated or freed.
+ * Arguments, arithmetic and results are those of
+ * rgc_gqa_attn_decode_rope_append, bit for bit.  A shape whose partials
+ * need more than 16 MiB (rgc_gqa_attn_decode_workspace_size(B, Hq, Hkv, D,
+ * max_len) > 16 MiB; at head dim 128 that is about 32,000 (sequence, query
+ * head, 128-key chunk) triples) returns RGC_ERR_WORKSPACE and launches
+ * nothing.  Every call on one GPU shares its array and leaves its partials
+ * there: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  RGC_ERR_HIP when the
+ * array's address cannot be obtained.
+ */
+int rgc_gqa_attn_decode_rope_append_static(void* o, const void* q, const void* k_new,
+                                           const void* v_new, void* k_cache, void* v_cache,
+                                           int dtype, int B, int Hq, int Hkv, int D, int S_max,
+                                           int64_t q_sb, int64_t q_sh, int64_t n_sb, int64_t n_sh,
+                                           int64_t o_sb, int64_t o_sh, int64_t kv_sb,
+                                           int64_t kv_sh, int64_t kv_ss, const int32_t* seq_lens,
+                                           int max_len, double base, int style, float scale,
+                                           float* lse, int32_t* err_flag, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ __all__ = [
     "RgcError", "library", "rope_apply", "kv_cache_append", "rope_append", "norm_rope_append",
     "gqa_attn_prefill",
     "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace", "diff_attn_prefill",
-    "gqa_attn_decode_rope_append",
+    "gqa_attn_decode_rope_append", "gqa_attn_decode_rope_append_static",
     "gqa_attn_prefill_varlen", "rope_backward", "gqa_attn_backward", "backward_workspace",
     "ROPE_HALF", "ROPE_INTERLEAVED", "timed_library", "kernel_timing", "timing_report",
 ]
@@ -72,6 +72,9 @@ _SIGNATURES = {
     "rgc_gqa_attn_decode_rope_append": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                              _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                              _p, _i, _d, _i, _f, _p, _sz, _p, _p, _p]),
+    "rgc_gqa_attn_decode_rope_append_static": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                                    _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                    _p, _i, _d, _i, _f, _p, _p, _p]),
 }
 
 _TIMING_SIGNATURES = {
@@ -414,6 +417,21 @@ def gqa_attn_decode_rope_append(q, k_new, v_new, k_cache, v_cache, seq_lens, max
         workspace = decode_workspace(B, Hq, Hkv, D, max_len, q.device)
     _call("rgc_gqa_attn_decode_rope_append", *args, float(base), int(style), float(scale), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _ptr(lse), _ptr(err_flag), _stream(q))
+    return o
+
+
+def gqa_attn_decode_rope_append_static(q, k_new, v_new, k_cache, v_cache, seq_lens, max_len=None,
+                                       base=10000.0, style=ROPE_HALF, scale=None, out=None, lse=None,
+                                       err_flag=None):
+    """gqa_attn_decode_rope_append with the partials in the library's own
+    per-GPU array (16 MiB) instead of a workspace: the library allocates
+    nothing.  Calls that overlap in time on one GPU race."""
+    o, args, _ = _decode_rope_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, max_len, out, lse,
+                                          err_flag)
+    if scale is None:
+        scale = q.shape[2] ** -0.5
+    _call("rgc_gqa_attn_decode_rope_append_static", *args, float(base), int(style), float(scale), _ptr(lse),
+          _ptr(err_flag), _stream(q))
     return o
 
 

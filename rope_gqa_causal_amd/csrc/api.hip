@@ -477,12 +477,13 @@ int rgc_gqa_attn_decode(void* o, const void* q, const void* k_cache, const void*
 
 namespace {
 
-// The one-launch step.
+// The one-launch step; with use_static the partials go to the library's own
+// per-GPU array instead of a caller workspace (nothing is allocated).
 int decode_rope_append_impl(void* o, const void* q, const void* k_new, const void* v_new, void* k_cache,
                             void* v_cache, int dtype, int B, int Hq, int Hkv, int D, int S_max, int64_t q_sb,
                             int64_t q_sh, int64_t n_sb, int64_t n_sh, int64_t o_sb, int64_t o_sh, int64_t kv_sb,
                             int64_t kv_sh, int64_t kv_ss, const int32_t* seq_lens, int max_len, double base,
-                            int style, float scale, void* workspace, size_t ws_bytes, float* lse,
+                            int style, float scale, void* workspace, size_t ws_bytes, bool use_static, float* lse,
                             int32_t* err_flag, void* stream) {
   int st = check_attn_common(dtype, B, 1, Hq, Hkv, D, S_max);
   if (st != RGC_OK) return st;
@@ -501,8 +502,13 @@ int decode_rope_append_impl(void* o, const void* q, const void* k_new, const voi
       !stride_ok(kv_sh, dtype) || !stride_ok(kv_ss, dtype))
     return RGC_ERR_LAYOUT;
   const size_t need = decode_workspace_bytes(B, Hq, Hkv, D, max_len);
-  if (!workspace || ws_bytes < need) return RGC_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RGC_ERR_LAYOUT;
+  if (use_static) {
+    if (need > kDecodeStaticScratchBytes) return RGC_ERR_WORKSPACE;
+    if (decode_static_scratch(&workspace) != hipSuccess) return RGC_ERR_HIP;
+  } else {
+    if (!workspace || ws_bytes < need) return RGC_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RGC_ERR_LAYOUT;
+  }
   AttnParams p = {};
   p.o = o;
   p.q = q;
@@ -549,7 +555,19 @@ int rgc_gqa_attn_decode_rope_append(void* o, const void* q, const void* k_new, c
                                     void* stream) {
   return decode_rope_append_impl(o, q, k_new, v_new, k_cache, v_cache, dtype, B, Hq, Hkv, D, S_max, q_sb, q_sh,
                                  n_sb, n_sh, o_sb, o_sh, kv_sb, kv_sh, kv_ss, seq_lens, max_len, base, style,
-                                 scale, workspace, ws_bytes, lse, err_flag, stream);
+                                 scale, workspace, ws_bytes, false, lse, err_flag, stream);
+}
+
+int rgc_gqa_attn_decode_rope_append_static(void* o, const void* q, const void* k_new, const void* v_new,
+                                           void* k_cache, void* v_cache, int dtype, int B, int Hq, int Hkv,
+                                           int D, int S_max, int64_t q_sb, int64_t q_sh, int64_t n_sb,
+                                           int64_t n_sh, int64_t o_sb, int64_t o_sh, int64_t kv_sb,
+                                           int64_t kv_sh, int64_t kv_ss, const int32_t* seq_lens, int max_len,
+                                           double base, int style, float scale, float* lse, int32_t* err_flag,
+                                           void* stream) {
+  return decode_rope_append_impl(o, q, k_new, v_new, k_cache, v_cache, dtype, B, Hq, Hkv, D, S_max, q_sb, q_sh,
+                                 n_sb, n_sh, o_sb, o_sh, kv_sb, kv_sh, kv_ss, seq_lens, max_len, base, style,
+                                 scale, nullptr, 0, true, lse, err_flag, stream);
 }
 
 }  // extern "C"

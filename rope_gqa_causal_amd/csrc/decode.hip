@@ -37,6 +37,8 @@
 //    (Merging inside the first kernel, by the last chunk to arrive, would
 //    need device-scope fences, and on gfx950 each of those writes back and
 //    invalidates the XCD's L2: measured 16x slower than the second launch.)
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "rope_math.h"
@@ -854,6 +856,36 @@ hipError_t launch_decode(const AttnParams& p, const DecodeRope& r, void* workspa
 }
 
 }  // namespace
+
+// The decode's partials in a library-owned device array, for callers that
+// cannot allocate a workspace.  Each GPU holds its own copy of `scratch`
+// (device code objects are loaded per device); the host needs that copy's
+// device address, which hipGetSymbolAddress gives once per device with the
+// device current.  The array's name itself is a host-side stand-in and is
+// never passed to a kernel.
+namespace {
+__device__ __align__(256) char scratch[kDecodeStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_static_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const AttnParams& p, void* workspace, hipStream_t stream) {
   return launch_decode<false>(p, DecodeRope{}, workspace, stream);

@@ -156,5 +156,11 @@ struct DecodeRope {
 };
 hipError_t launch_decode_rope_bf16(const AttnParams& p, const DecodeRope& r, void* ws, hipStream_t stream);
 
+// A decode workspace the library owns, for callers that cannot allocate:
+// a file-scope device array of kDecodeStaticScratchBytes per GPU.  Returns
+// the current device's copy (its address is looked up once per device).
+// Every call on one GPU shares it, so calls that overlap on a GPU race.
+constexpr size_t kDecodeStaticScratchBytes = size_t(16) << 20;
+hipError_t decode_static_scratch(void** ptr);
 
 }  // namespace rgc

@@ -270,3 +270,30 @@ def test_attention_entries_reject_a_scale_that_is_not_positive_and_finite(scale)
     assert _bwd(scale=scale) == ARG
     assert _decode(scale=scale) == ARG
     assert _decode_rope(scale=scale) == ARG
+
+
+def _decode_static(**kw):
+    a = dict(o=A, q=A, kn=A, vn=A, k=A, v=A, dt=BF16, B=2, Hq=4, Hkv=2, D=64, S_max=32, q_sb=256, q_sh=64,
+             n_sb=128, n_sh=64, o_sb=256, o_sh=64, kv_sb=2 * 32 * 64, kv_sh=32 * 64, kv_ss=64, lens=A,
+             max_len=32, base=10000.0, style=0, scale=0.125, lse=None, err=None)
+    a.update(kw)
+    return rgc.library().rgc_gqa_attn_decode_rope_append_static(
+        a["o"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["D"],
+        a["S_max"], a["q_sb"], a["q_sh"], a["n_sb"], a["n_sh"], a["o_sb"], a["o_sh"], a["kv_sb"], a["kv_sh"],
+        a["kv_ss"], a["lens"], a["max_len"], a["base"], a["style"], a["scale"], a["lse"], a["err"], None)
+
+
+def test_allocation_free_decode_step_checks_its_arguments_and_its_array_size():
+    lib = rgc.library()
+    assert _decode_static(dt=F32) == DTYPE
+    assert _decode_static(scale=0.0) == ARG
+    assert _decode_static(kn=None) == NULL
+    assert _decode_static(max_len=33) == CAPACITY
+    assert _decode_static(B=0) == OK
+    # partials beyond the 16 MiB array: refused before anything is launched
+    big = dict(B=64, Hq=64, Hkv=8, D=128, S_max=8192, max_len=8192, q_sb=64 * 128, o_sb=64 * 128,
+               n_sb=8 * 128, kv_sb=8 * 8192 * 128, kv_sh=8192 * 128, kv_ss=128, q_sh=128, o_sh=128, n_sh=128)
+    assert lib.rgc_gqa_attn_decode_workspace_size(64, 64, 8, 128, 8192) > 16 << 20
+    assert _decode_static(**big) == WORKSPACE
+    # the ragged-decode shape fits
+    assert lib.rgc_gqa_attn_decode_workspace_size(64, 24, 8, 128, 2080) <= 16 << 20
