@@ -190,15 +190,21 @@ def summarize_counters(run_dirs):
                 if short not in ("prefill_kernel", "mfma_bf16_kernel"):
                     continue
                 key = (path, did)
-                per.setdefault(short, {}).setdefault(cname, {}).setdefault(key, 0.0)
-                per[short][cname][key] += val
+                d = per.setdefault(short, {}).setdefault(cname, {})
+                # GRBM counters repeat one GPU-wide count per XCD: take the
+                # largest (as the profiler's own derived formulas do); SQ
+                # counters are summed over their instances.
+                if cname.startswith("GRBM_"):
+                    d[key] = max(d.get(key, 0.0), val)
+                else:
+                    d[key] = d.get(key, 0.0) + val
     avg = {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in per.items()}
     pre = avg.get("prefill_kernel", {})
     cal = avg.get("mfma_bf16_kernel", {})
 
     def busy(a):
         if "SQ_VALU_MFMA_BUSY_CYCLES" in a and a.get("GRBM_GUI_ACTIVE"):
-            return a["SQ_VALU_MFMA_BUSY_CYCLES"] / (a["GRBM_GUI_ACTIVE"] * 256 * 4)
+            return a["SQ_VALU_MFMA_BUSY_CYCLES"] / (a["GRBM_GUI_ACTIVE"] * 256 * 4)  # 1024 SIMDs
         return None
     derived = {"mfma_busy": busy(pre), "mfma_busy_calibration_loop": busy(cal)}
     if derived["mfma_busy"] is not None and derived["mfma_busy_calibration_loop"]:
@@ -207,6 +213,11 @@ def summarize_counters(run_dirs):
         derived["executed_mfma_flops"] = pre["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
     if pre.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in pre:
         derived["valu_per_mfma"] = pre["SQ_INSTS_VALU"] / pre["SQ_INSTS_MFMA"]
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in pre and pre.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+        derived["valu_coexec_per_mfma_busy"] = pre["SQ_VALU_MFMA_COEXEC_CYCLES"] / pre["SQ_VALU_MFMA_BUSY_CYCLES"]
+    if "SQ_ACTIVE_INST_VALU" in pre and pre.get("GRBM_GUI_ACTIVE"):
+        # the profiler's VALUBusy formula (as a fraction)
+        derived["valu_busy"] = pre["SQ_ACTIVE_INST_VALU"] / 256 / pre["GRBM_GUI_ACTIVE"]
     if pre.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in pre:
         derived["lds_conflict_per_active"] = pre["SQ_LDS_BANK_CONFLICT"] / pre["SQ_LDS_IDX_ACTIVE"]
     derived = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in derived.items()}
@@ -370,26 +381,29 @@ def ceilings(iters=10):
         return {"error": "ceilings/libceil.so is not built"}
     lib = ctypes.CDLL(path)
     lib.ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                     ctypes.c_void_p]
+                                     ctypes.c_int, ctypes.c_void_p]
     lib.ceil_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     nbytes = 2 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     best_read = 0.0
     read_rows = []
-    for wgs in (1024, 2048, 4096, 8192):
+    modes = {0: "grid-stride, 4 loads in flight", 1: "contiguous slices, 8 in flight",
+             2: "contiguous slices, 16 in flight", 3: "contiguous slices, 8 in flight, nontemporal"}
+    for mode, wgs in ((0, 2048), (1, 1024), (1, 2048), (1, 4096), (2, 1024), (2, 2048), (3, 2048)):
         out = torch.empty(wgs * 256, dtype=torch.int32, device="cuda")
-        if lib.ceil_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()), wgs, stream):
+        args = (ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()), wgs, mode, stream)
+        if lib.ceil_stream_read(*args):
             return {"error": "ceil_stream_read refused"}
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(iters):
-            lib.ceil_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()), wgs, stream)
+            lib.ceil_stream_read(*args)
         e1.record()
         torch.cuda.synchronize()
         gbs = nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        read_rows.append({"workgroups": wgs, "GB/s": round(gbs, 1)})
+        read_rows.append({"form": modes[mode], "workgroups": wgs, "GB/s": round(gbs, 1)})
         best_read = max(best_read, gbs)
     del buf
     mf_rows, best_mf = [], 0.0
@@ -411,8 +425,9 @@ def ceilings(iters=10):
             "hbm_read_runs": read_rows,
             "mfma_bf16_TFLOPs": round(best_mf, 1), "mfma_bf16_frac_of_spec": round(best_mf / BF16_PEAK_TFLOPS, 4),
             "mfma_runs": mf_rows,
-            "kernels": "ceilings/ceilings.hip: grid-stride 16-byte reads of 2 GiB (4 loads in flight per lane); "
-                       "v_mfma_f32_32x32x16_bf16 back to back on 4 accumulators per wave, no memory traffic"}
+            "kernels": "ceilings/ceilings.hip: 16-byte reads of a 2 GiB buffer (8x the MALL) in several forms, "
+                       "the best reported; v_mfma_f32_32x32x16_bf16 back to back on 4 accumulators per wave, no "
+                       "memory traffic"}
 
 
 class Diff:
@@ -866,10 +881,13 @@ def main():
         op_achieved = bytes_avg / (op_avg * 1e-3) / 1e9
         # The split kernel alone: the instrumented build times each kernel
         # of one more (untimed) decode phase.
-        rgc.timing_report()  # clear
-        with rgc.kernel_timing():
-            dec.run()
-        torch.cuda.synchronize()
+        # The first phase through the instrumented build loads its code
+        # objects; it is run once and its record dropped.
+        for _ in range(2):
+            rgc.timing_report()  # clear
+            with rgc.kernel_timing():
+                dec.run()
+            torch.cuda.synchronize()
         kt = rgc.timing_report()
         n_split, split_us = kt["decode_split_kernel"]
         n_comb, comb_us = kt.get("decode_combine_kernel", (n_split, 0.0))

@@ -21,6 +21,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+__device__ __forceinline__ uint32_t fold(u32x4 a) { return a[0] ^ a[1] ^ a[2] ^ a[3]; }
+
+// Grid-stride form: consecutive lanes of the whole grid read consecutive
+// 16-byte pieces, four pieces in flight per lane.
 __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restrict__ src, size_t n16,
                                                           uint32_t* __restrict__ out) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -28,13 +32,32 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restric
   uint32_t acc = 0;
   for (; i + 3 * stride < n16; i += 4 * stride) {
     const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
-    acc ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+    acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
   }
-  for (; i < n16; i += stride) {
-    const u32x4 a = src[i];
-    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  for (; i < n16; i += stride) acc ^= fold(src[i]);
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// Contiguous form: workgroup w owns the w-th slice of the buffer and walks
+// it in blocks of 256 lanes x U pieces (U 16-byte loads in flight per lane,
+// 4 KiB contiguous per load instruction of the workgroup).  NT: the loads
+// carry the nontemporal hint.
+template <int U, bool NT>
+__global__ void __launch_bounds__(256) stream_read_chunk_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                                uint32_t* __restrict__ out) {
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
+  uint32_t acc = 0;
+  size_t i = lo + threadIdx.x;
+  for (; i + (U - 1) * 256 < hi; i += U * 256) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = NT ? __builtin_nontemporal_load(src + i + u * 256) : src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= fold(v[u]);
   }
+  for (; i < hi; i += 256) acc ^= fold(src[i]);
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
@@ -61,12 +84,21 @@ __global__ void __launch_bounds__(256) mfma_bf16_kernel(float* __restrict__ out,
 extern "C" {
 
 // Reads `bytes` (a multiple of 16) from src with `wgs` workgroups of 256
-// threads; out receives wgs * 256 words.  0, or -1 for a bad argument, or
-// -9 when the launch is refused.
-int ceil_stream_read(const void* src, size_t bytes, uint32_t* out, int wgs, void* stream) {
-  if (!src || !out || wgs <= 0 || bytes % 16 != 0) return -1;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream,
-                     (const u32x4*)src, bytes / 16, out);
+// threads; out receives wgs * 256 words.  mode 0: grid-stride, 4 loads in
+// flight per lane; 1, 2: contiguous slices with 8 or 16 loads in flight;
+// 3: as 1 with nontemporal loads.  0, or -1 for a bad argument, or -9 when
+// the launch is refused.
+int ceil_stream_read(const void* src, size_t bytes, uint32_t* out, int wgs, int mode, void* stream) {
+  if (!src || !out || wgs <= 0 || bytes % 16 != 0 || mode < 0 || mode > 3) return -1;
+  const u32x4* s = (const u32x4*)src;
+  const size_t n = bytes / 16;
+  hipStream_t st = (hipStream_t)stream;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(stream_read_kernel, dim3(wgs), dim3(256), 0, st, s, n, out); break;
+    case 1: hipLaunchKernelGGL((stream_read_chunk_kernel<8, false>), dim3(wgs), dim3(256), 0, st, s, n, out); break;
+    case 2: hipLaunchKernelGGL((stream_read_chunk_kernel<16, false>), dim3(wgs), dim3(256), 0, st, s, n, out); break;
+    default: hipLaunchKernelGGL((stream_read_chunk_kernel<8, true>), dim3(wgs), dim3(256), 0, st, s, n, out); break;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -9;
 }
 

@@ -227,12 +227,12 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
       const int key = min(kw + ps * KPP + key_sub, L - 1);
       const bf16_t* kr = kbase + (int64_t)key * p.kv_ss;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kf[ps][i] = ld16(kr + 8 * (part + LPK * i));
+      for (int i = 0; i < 4; ++i) kf[ps][i] = ld16_nt(kr + 8 * (part + LPK * i));
     }
 #pragma unroll
     for (int t = 0; t < VLOADS; ++t) {
       const int key = min(kw + t * KPI + kq, L - 1);
-      vf[t] = ld16(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
+      vf[t] = ld16_nt(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
 
@@ -465,12 +465,12 @@ __global__ void __launch_bounds__(64 * W) decode_loop_kernel(AttnParams p, int n
       const int key = min(kw + ps * KPP + key_sub, L - 1);
       const bf16_t* kr = kbase + (int64_t)key * p.kv_ss;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kf[ps][i] = ld16(kr + 8 * (part + LPK * i));
+      for (int i = 0; i < 4; ++i) kf[ps][i] = ld16_nt(kr + 8 * (part + LPK * i));
     }
 #pragma unroll
     for (int t = 0; t < VLOADS; ++t) {
       const int key = min(kw + t * KPI + kq, L - 1);
-      vf[t] = ld16(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
+      vf[t] = ld16_nt(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
     }
   };
   // q (with ROPE: the lane's theta, the q and new-k pairs -- lanes past D/2
