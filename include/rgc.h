@@ -293,6 +293,39 @@ int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2,
                           int32_t* err_flag, void* stream);
 
 /*
+ * rgc_diff_attn_decode -- cached decode of differential attention (page
+ * "750美元从零训练3个LLM：一位开发者的实战复盘", section "V2：引入前沿技术"):
+ * one new query row per sequence,
+ *   o = softmax(scale q1 K1^T) V - lambda softmax(scale q2 K2^T) V
+ * over the L = seq_lens[b] cached slots of its KV head h / (Hq/Hkv).
+ *   o          [B,Hq,D] bf16, strides (o_sb, o_sh); written.
+ *   q1, q2     [B,Hq,D] bf16, both with strides (q_sb, q_sh); already
+ *              rotated when RoPE is used.
+ *   k1_cache, k2_cache, v_cache  [B,Hkv,S_max,D] bf16, all three with strides
+ *              (kv_sb, kv_sh, kv_ss); the value head dim equals D.
+ *   seq_lens   [B] int32: cache length including the new token (slot L-1
+ *              is the query's own position); max_len as in
+ *              rgc_gqa_attn_decode.
+ *   lambda     the constant weight of the second map; scale as for the
+ *              other attention calls.
+ *   workspace  >= rgc_diff_attn_decode_workspace_size(B, Hq, Hkv, D,
+ *              max_len) bytes, 256-byte aligned, caller-owned; its contents
+ *              need no initialisation.  Calls that overlap in time must use
+ *              different workspaces.
+ * bf16 only (RGC_ERR_DTYPE); head dim 32, 64 or 128.  Each map is split
+ * along the cache length, merged by max-rescaled sums, normalised by its own
+ * sum of weights (fp32), and o is rounded once.  A sequence with seq_lens
+ * outside [1, min(max_len, S_max)] gets NaN rows and the flag.
+ */
+size_t rgc_diff_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_len);
+int rgc_diff_attn_decode(void* o, const void* q1, const void* q2, const void* k1_cache,
+                         const void* k2_cache, const void* v_cache, int dtype, int B, int Hq,
+                         int Hkv, int D, int S_max, int64_t q_sb, int64_t q_sh, int64_t o_sb,
+                         int64_t o_sh, int64_t kv_sb, int64_t kv_sh, int64_t kv_ss,
+                         const int32_t* seq_lens, int max_len, float lambda, float scale,
+                         void* workspace, size_t ws_bytes, int32_t* err_flag, void* stream);
+
+/*
  * Bytes of device workspace rgc_gqa_attn_decode needs for this shape
  * (max_len: the largest length it will be called with).  0 for an invalid
  * shape.

@@ -25,7 +25,8 @@ __all__ = [
     "RgcError", "library", "rope_apply", "kv_cache_append", "rope_append", "norm_rope_append",
     "gqa_attn_prefill",
     "gqa_attn_decode", "gqa_attn_decode_workspace_size", "decode_workspace", "diff_attn_prefill",
-    "gqa_attn_decode_rope_append", "gqa_attn_decode_rope_append_static",
+    "gqa_attn_decode_rope_append", "gqa_attn_decode_rope_append_static", "diff_attn_decode",
+    "diff_decode_workspace",
     "gqa_attn_prefill_varlen", "rope_backward", "gqa_attn_backward", "backward_workspace",
     "ROPE_HALF", "ROPE_INTERLEAVED", "timed_library", "kernel_timing", "timing_report",
 ]
@@ -66,6 +67,10 @@ _SIGNATURES = {
                                    _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                    _p, _f, _f, _p, _p]),
     "rgc_gqa_attn_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "rgc_diff_attn_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "rgc_diff_attn_decode": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                  _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  _p, _i, _f, _f, _p, _sz, _p, _p]),
     "rgc_gqa_attn_decode": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                  _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                  _p, _i, _f, _p, _sz, _p, _p, _p]),
@@ -365,6 +370,39 @@ def diff_attn_prefill(q1, q2, k1_cache, k2_cache, v_cache, lam, q_start=None, sc
           o.stride(0), o.stride(1), o.stride(2),
           k1_cache.stride(0), k1_cache.stride(1), k1_cache.stride(2),
           _ptr(q_start), float(lam), float(scale), _ptr(err_flag), _stream(q1))
+    return o
+
+
+def diff_decode_workspace(B, Hq, Hkv, D, max_len, device="cuda"):
+    """A workspace tensor large enough for diff_attn_decode."""
+    n = max(int(library().rgc_diff_attn_decode_workspace_size(B, Hq, Hkv, D, max_len)), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def diff_attn_decode(q1, q2, k1_cache, k2_cache, v_cache, seq_lens, lam, max_len=None, workspace=None,
+                     scale=None, out=None, err_flag=None):
+    """Cached differential decode: q1, q2 [B,Hq,D] (same strides) over caches
+    [B,Hkv,S_max,D] (same strides) of lengths seq_lens[b]; bf16."""
+    _gpu(q1, q2, k1_cache, k2_cache, v_cache, seq_lens, workspace, out, err_flag)
+    B, Hq, D = q1.shape
+    _, Hkv, S_max, _ = k1_cache.shape
+    if q2.shape != q1.shape or q2.stride() != q1.stride():
+        raise ValueError("q1 and q2 must share shape and strides")
+    if (k2_cache.shape != k1_cache.shape or v_cache.shape != k1_cache.shape
+            or k2_cache.stride() != k1_cache.stride() or v_cache.stride() != k1_cache.stride()):
+        raise ValueError("k1, k2 and v caches must share shape and strides")
+    if scale is None:
+        scale = D ** -0.5
+    if max_len is None:
+        max_len = S_max
+    if workspace is None:
+        workspace = diff_decode_workspace(B, Hq, Hkv, D, max_len, q1.device)
+    o = torch.empty_like(q1) if out is None else out
+    seq_lens = _lens(seq_lens, B, "seq_lens")
+    _call("rgc_diff_attn_decode", _ptr(o), _ptr(q1), _ptr(q2), _ptr(k1_cache), _ptr(k2_cache), _ptr(v_cache),
+          _dtype(q1), B, Hq, Hkv, D, S_max, q1.stride(0), q1.stride(1), o.stride(0), o.stride(1),
+          k1_cache.stride(0), k1_cache.stride(1), k1_cache.stride(2), _ptr(seq_lens), int(max_len), float(lam),
+          float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(err_flag), _stream(q1))
     return o
 
 

@@ -418,6 +418,61 @@ int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2, const void* k
   return hip_status(launch_diff_bf16(dp, reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t rgc_diff_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_len) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || !headdim_ok(D) || max_len < 1) return 0;
+  return diff_decode_workspace_bytes(B, Hq, D, max_len);
+}
+
+int rgc_diff_attn_decode(void* o, const void* q1, const void* q2, const void* k1_cache, const void* k2_cache,
+                         const void* v_cache, int dtype, int B, int Hq, int Hkv, int D, int S_max, int64_t q_sb,
+                         int64_t q_sh, int64_t o_sb, int64_t o_sh, int64_t kv_sb, int64_t kv_sh, int64_t kv_ss,
+                         const int32_t* seq_lens, int max_len, float lambda, float scale, void* workspace,
+                         size_t ws_bytes, int32_t* err_flag, void* stream) {
+  int st = check_attn_common(dtype, B, 1, Hq, Hkv, D, S_max);
+  if (st != RGC_OK) return st;
+  if (dtype != RGC_BF16) return RGC_ERR_DTYPE;
+  if (B == 0) return RGC_OK;
+  if (!o || !q1 || !q2 || !k1_cache || !k2_cache || !v_cache || !seq_lens) return RGC_ERR_NULL;
+  if (max_len < 1 || max_len > S_max) return RGC_ERR_CAPACITY;
+  if (!(scale > 0.f) || !std::isfinite(scale) || !std::isfinite(lambda)) return RGC_ERR_ARG;
+  if (!aligned16(o) || !aligned16(q1) || !aligned16(q2) || !aligned16(k1_cache) || !aligned16(k2_cache) ||
+      !aligned16(v_cache))
+    return RGC_ERR_LAYOUT;
+  if (!stride_ok(q_sb, dtype) || !stride_ok(q_sh, dtype) || !stride_ok(o_sb, dtype) || !stride_ok(o_sh, dtype) ||
+      !stride_ok(kv_sb, dtype) || !stride_ok(kv_sh, dtype) || !stride_ok(kv_ss, dtype))
+    return RGC_ERR_LAYOUT;
+  const size_t need = diff_decode_workspace_bytes(B, Hq, D, max_len);
+  if (!workspace || ws_bytes < need) return RGC_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RGC_ERR_LAYOUT;
+  DiffParams dp = {};
+  AttnParams& p = dp.a;
+  p.o = o;
+  p.q = q1;
+  p.k = k1_cache;
+  p.v = v_cache;
+  p.B = B;
+  p.Sq = 1;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.S_max = S_max;
+  p.q_sb = q_sb;
+  p.q_sh = q_sh;
+  p.o_sb = o_sb;
+  p.o_sh = o_sh;
+  p.kv_sb = kv_sb;
+  p.kv_sh = kv_sh;
+  p.kv_ss = kv_ss;
+  p.seq_lens = seq_lens;
+  p.max_len = max_len;
+  p.scale = scale;
+  p.err = err_flag;
+  dp.q2 = q2;
+  dp.k2 = k2_cache;
+  dp.lambda = lambda;
+  return hip_status(launch_diff_decode_bf16(dp, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t rgc_gqa_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_len) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || !headdim_ok(D) || max_len < 1) return 0;
   return decode_workspace_bytes(B, Hq, Hkv, D, max_len);

@@ -48,6 +48,18 @@ __device__ __forceinline__ float sum_within(float x) {
   return x;
 }
 
+// Sum over the LPR lanes of one row group (lanes that differ in the bits
+// below LPR: xor 1, 2, 4, 8 within a 16-lane row, xor 16, 32 across).
+template <int LPR>
+__device__ __forceinline__ float sum_within_row(float x) {
+  if (LPR >= 2) x += dpp<0xB1>(x);                // quad_perm [1,0,3,2]
+  if (LPR >= 4) x += dpp<0x4E>(x);                // quad_perm [2,3,0,1]
+  if (LPR >= 8) x += dpp<0x141>(x);               // row_half_mirror
+  if (LPR >= 16) x += dpp<0x140>(x);              // row_mirror
+  if (LPR >= 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                          __builtin_bit_cast(bf16x2, b), c, false);

@@ -115,6 +115,10 @@ struct DiffParams {
   float lambda;
 };
 hipError_t launch_diff_bf16(const DiffParams& p, hipStream_t stream);
+// Cached decode of differential attention: a.seq_lens and a.max_len as in
+// the decode; the caller's workspace holds both maps' chunk partials.
+size_t diff_decode_workspace_bytes(int B, int Hq, int D, int max_len);
+hipError_t launch_diff_decode_bf16(const DiffParams& p, void* ws, hipStream_t stream);
 
 // Gradients of causal GQA self-attention: q, o, dO, dq share one layout
 // [B,S,Hq,D]; k, v, dk, dv share [B,S,Hkv,D]; lse [B,Hq,S] from the forward.

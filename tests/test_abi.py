@@ -297,3 +297,34 @@ def test_allocation_free_decode_step_checks_its_arguments_and_its_array_size():
     assert _decode_static(**big) == WORKSPACE
     # the ragged-decode shape fits
     assert lib.rgc_gqa_attn_decode_workspace_size(64, 24, 8, 128, 2080) <= 16 << 20
+
+
+def _diff_decode(**kw):
+    a = dict(o=A, q1=A, q2=A, k1=A, k2=A, v=A, dt=BF16, B=2, Hq=4, Hkv=2, D=64, S_max=32, q_sb=256, q_sh=64,
+             o_sb=256, o_sh=64, kv_sb=2 * 32 * 64, kv_sh=32 * 64, kv_ss=64, lens=A, max_len=32, lam=0.8,
+             scale=0.125, ws=A, ws_bytes=1 << 20, err=None)
+    a.update(kw)
+    return rgc.library().rgc_diff_attn_decode(
+        a["o"], a["q1"], a["q2"], a["k1"], a["k2"], a["v"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["D"],
+        a["S_max"], a["q_sb"], a["q_sh"], a["o_sb"], a["o_sh"], a["kv_sb"], a["kv_sh"], a["kv_ss"], a["lens"],
+        a["max_len"], a["lam"], a["scale"], a["ws"], a["ws_bytes"], a["err"], None)
+
+
+def test_diff_decode_rejects_bad_arguments_before_launch():
+    lib = rgc.library()
+    assert _diff_decode(Hq=3) == GROUP
+    assert _diff_decode(dt=F32) == DTYPE
+    assert _diff_decode(D=96) == HEADDIM
+    assert _diff_decode(q2=None) == NULL
+    assert _diff_decode(lens=None) == NULL
+    assert _diff_decode(k2=A + 8) == LAYOUT
+    assert _diff_decode(kv_ss=68) == LAYOUT
+    assert _diff_decode(max_len=33) == CAPACITY
+    assert _diff_decode(lam=float("nan")) == ARG
+    assert _diff_decode(scale=0.0) == ARG
+    assert _diff_decode(ws=None) == WORKSPACE
+    assert _diff_decode(ws_bytes=16) == WORKSPACE
+    assert _diff_decode(ws=A + 16) == LAYOUT
+    assert _diff_decode(B=0) == OK
+    assert 0 < lib.rgc_diff_attn_decode_workspace_size(4, 16, 8, 64, 128) < \
+        lib.rgc_diff_attn_decode_workspace_size(4, 16, 8, 64, 1024)

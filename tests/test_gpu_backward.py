@@ -60,6 +60,20 @@ def test_backward_on_the_3p8b_layout_sampled():
     assert_close_grad(dq[:1], rq, "dq")
 
 
+def test_backward_at_the_bench_shape_sampled():
+    # The batch the bench times (8 x 2048 tokens, 24 q / 8 KV, D 128), in
+    # that launch configuration; the oracle's exact backward runs on one
+    # sequence (the gradients of different sequences are independent).
+    B, S, Hq, Hkv, D = 8, 2048, 24, 8, 128
+    q, k, v, d_o, qg, kg, vg, o, lse = _forward(B, S, Hq, Hkv, D, 303)
+    dq, dk, dv = rgc.gqa_attn_backward(qg, kg, vg, o, d_o.cuda(), lse)
+    b = 5
+    rq, rk, rv = oracle.attn_backward(q[b:b + 1], k[b:b + 1], v[b:b + 1], d_o[b:b + 1])
+    assert_close_grad(dv[b:b + 1], rv, "dv")
+    assert_close_grad(dk[b:b + 1], rk, "dk")
+    assert_close_grad(dq[b:b + 1], rq, "dq")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("style", [rgc.ROPE_HALF, rgc.ROPE_INTERLEAVED])
 def test_rope_backward_matches_the_oracle_and_undoes_the_rotation(dtype, style):

@@ -130,3 +130,35 @@ def test_fused_step_on_the_ragged_decode_workload():
     for b in [0, 17, 63, int(torch.argmax(lens)), int(torch.argmin(lens))]:
         ref = oracle.attn_decode(q_r[b:b + 1], kc_ref[b:b + 1], vc_b[b:b + 1].cpu(), lens[b:b + 1])
         assert_close(o_b[b:b + 1], ref, torch.bfloat16, f"fused ragged step b={b} L={int(lens[b])}")
+
+
+@pytest.mark.parametrize("style", [rgc.ROPE_HALF, rgc.ROPE_INTERLEAVED])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("group", [1, 3, 8])
+def test_fused_split_step_equals_prologue_then_decode_bit_for_bit(style, D, group):
+    # 64 sequences of lengths up to 700 make more than 256 split workgroups,
+    # so both forms take the split kernel (not the one-workgroup walk): with
+    # group 8 two head subgroups share each new slot (only the first writes
+    # it), with group 1 and 3 one workgroup covers the group.  The new slots
+    # hold NaN canaries, so any read of a slot the step fills shows.
+    Hkv = 2
+    Hq = Hkv * group
+    S_max = 700
+    g = synth.generator(4000 + D + group + style)
+    lens = synth.lengths(64, 1, S_max, g)
+    lens[:6] = torch.tensor([1, 2, 128, 129, 256, 700], dtype=torch.int32)
+    B = lens.numel()
+    q, k_new, v_new, kc, vc = _inputs(B, Hq, Hkv, D, S_max, lens, seed=D * 10 + group + style + 77)
+    dev = [t.cuda() for t in (q, k_new, v_new, kc, vc)]
+    q_a, kn_a, vn_a, kc_a, vc_a = [t.clone() for t in dev]
+    q_b, kn_b, vn_b, kc_b, vc_b = [t.clone() for t in dev]
+    lens_g = lens.cuda()
+    lse_a = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    lse_b = torch.empty_like(lse_a)
+    o_a = _two_launch(q_a, kn_a, vn_a, kc_a, vc_a, lens_g, S_max, style, lse_a)
+    o_b = rgc.gqa_attn_decode_rope_append(q_b, kn_b, vn_b, kc_b, vc_b, lens_g, S_max, style=style, lse=lse_b)
+    assert torch.isfinite(o_b.float()).all(), "the fused step read a slot it was to fill"
+    assert torch.equal(o_a.cpu().view(I16), o_b.cpu().view(I16))
+    assert torch.equal(lse_a.cpu(), lse_b.cpu())
+    assert torch.equal(kc_a.cpu().view(I16), kc_b.cpu().view(I16))
+    assert torch.equal(vc_a.cpu().view(I16), vc_b.cpu().view(I16))

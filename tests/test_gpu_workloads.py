@@ -118,14 +118,15 @@ def test_llama125m_layer_end_to_end_one_launch_steps():
     assert_close(dec, ref_dec, torch.bfloat16, "125m one-launch decode steps")
 
 
-def test_prefill3p8b_full_size_sampled_rows():
+@pytest.mark.parametrize("seed_off", [0, 100, 200])
+def test_prefill3p8b_full_size_sampled_rows(seed_off):
     w = synth.WORKLOADS["prefill3p8b"]
-    g = synth.generator(w.seed)
+    g = synth.generator(w.seed + seed_off)
     q, k, v = synth.qkv(w.B, w.S, w.Hq, w.Hkv, w.D, g, w.dtype)
     kc = k.transpose(1, 2).contiguous()
     vc = v.transpose(1, 2).contiguous()
     o = rgc.gqa_attn_prefill(q.cuda(), kc.cuda(), vc.cuda()).cpu()
-    sg = synth.generator(99)
+    sg = synth.generator(99 + seed_off)
     for b in range(w.B):
         s0 = int(torch.randint(0, w.S - 16, (1,), generator=sg))
         for lo in (s0, w.S - 16):
@@ -135,9 +136,10 @@ def test_prefill3p8b_full_size_sampled_rows():
             assert_close(o[b:b + 1, rows], ref, torch.bfloat16, f"3.8B b={b} rows {lo}")
 
 
-def test_ragged_decode_full_size_sampled_sequences():
+@pytest.mark.parametrize("seed_off", [0, 100, 200])
+def test_ragged_decode_full_size_sampled_sequences(seed_off):
     w = synth.WORKLOADS["ragged_decode"]
-    g = synth.generator(w.seed)
+    g = synth.generator(w.seed + seed_off)
     lens0 = synth.lengths(w.B, w.len_lo, w.len_hi, g)
     S_max = w.len_hi + w.steps
     kc, vc = synth.filled_cache(w.B, w.Hkv, S_max, w.D, g, w.dtype)
