@@ -8,35 +8,44 @@
 //
 // A dense contraction (QK^T then PV) on bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//  * a workgroup of 8 waves owns one query head and 256 query positions;
-//    each wave owns 32 positions.  Two waves share a SIMD (<= 256 registers
-//    each), so one wave's softmax (VALU) runs under the other's MFMAs;
+//  * a workgroup owns one KV head of one sequence and 256 query rows drawn
+//    from ALL the query heads of that KV head: rows are (position, head)
+//    pairs in position-major order, so every K/V tile the workgroup stages
+//    in LDS serves each query head of the group, and the 256 rows span only
+//    256/g positions (g = query heads per KV head), which keeps the causal
+//    extent of its eight waves within a tile of each other;
+//  * eight waves of 32 rows; waves w and w+4 share a SIMD.  The waves run a
+//    ping-pong schedule: every tile step is split into a matrix phase (the
+//    previous tile's O^T += V^T P^T and this tile's S^T = K Q^T, 32 MFMAs)
+//    and a vector phase (mask, online softmax, probabilities rounded to
+//    bf16), and waves 0-3 run their matrix phase while waves 4-7 run their
+//    vector phase and vice versa, with a workgroup barrier at every phase
+//    change.  The softmax of one wave thus issues beside the other wave's
+//    matrix instructions instead of between its own;
 //  * scores are computed transposed, S^T = K Q^T (keys in the MFMA M
 //    dimension): a lane holds one query's column, so the softmax max and sum
 //    are in-lane except one v_permlane32_swap with the lane 32 away, and the
 //    probabilities are already in the B-operand layout of O^T = V^T P^T --
 //    P never leaves registers;
 //  * 64-key K and V tiles are staged HBM -> registers -> LDS through a
-//    4-slot ring (tile j read, j+1 ready, j+2 written, j-1 still being read
-//    by slower waves), so one barrier per two tiles suffices; the global
-//    loads of tile j+2 are in flight while tile j is multiplied;
-//  * both tiles stay row-major in LDS with a per-row XOR swizzle of their
-//    16-byte chunks: K fragments (A operand of S^T) are conflict-free 16-byte
-//    reads, and V^T fragments (A operand of O^T) come straight from the
-//    row-major V tile through ds_read_b64_tr_b16, the gfx950 transposing LDS
-//    read -- V is never transposed in software;
-//  * the loop is unrolled over the ring so every LDS address is a per-lane
-//    base register plus an immediate offset, and tile loads use a scalar base
-//    plus a per-lane 32-bit offset: the VALU does softmax work only.  The
-//    causal mask is applied on diagonal tiles only;
+//    4-slot ring: tile k + 3 is fetched during tile k's vector phase and
+//    stored during tile k + 1's, so its loads are in flight across a whole
+//    matrix phase; the barriers carry no wait for them.  Both tiles stay
+//    row-major in LDS with a per-row XOR swizzle of their 16-byte chunks: K
+//    fragments (A operand of S^T) are conflict-free 16-byte reads, and V^T
+//    fragments (A operand of O^T) come straight from the row-major V tile
+//    through ds_read_b64_tr_b16, the gfx950 transposing LDS read;
 //  * the running max is only raised (and O rescaled) when a tile's max
 //    exceeds it by more than 2^8, so the rescale is almost never taken; p is
 //    then at most 256, exact in fp32 and within bf16 range.  The tile max
 //    itself is only computed when some lane's tile sum of p passes 2^8 (a
-//    necessary condition for a p past 2^8): a row block's first tile and the
+//    necessary condition for a p past 2^8): a wave's first tile and the
 //    rare raise -- the common tile does no max reduction at all;
-//  * tiles above a wave's causal diagonal are skipped, workgroups are
-//    issued heaviest q-tile first.
+//  * the causal mask is applied on diagonal tiles only; tiles past a wave's
+//    last row are skipped (the wave still keeps the barriers); workgroups
+//    are issued heaviest row block first, XCD-aware.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "mfma_attn.h"
@@ -48,10 +57,10 @@ constexpr float kLog2e = kAttnLog2e;
 constexpr float kLn2 = kAttnLn2;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;   // query positions per workgroup
-constexpr int kKT = 64;            // keys per tile
-constexpr int kSlots = 4;          // LDS ring: tile j read, j+1 ready, j+2 written, j-1 draining
-constexpr int kXcds = 8;           // MI355X: workgroup i is dispatched to XCD i % 8
+constexpr int kRows = 32 * kWaves;  // (position, head) rows per workgroup
+constexpr int kKT = 64;             // keys per tile
+constexpr int kSlots = 5;           // LDS ring (K and V tile per slot)
+constexpr int kXcds = 8;            // MI355X: workgroup i is dispatched to XCD i % 8
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kSumTrigger = 256.0f;      // 2^kRescaleThreshold
 
@@ -87,12 +96,32 @@ struct Tile {
   }
 };
 
-// Tile staging: wave w's i-th piece covers 1 KB of a slot contiguously (lane
-// l at byte 16l); the lane fetches the logical chunk stored there.
+// HBM -> LDS without registers: one global_load_lds_dwordx4 moves 16 bytes
+// per lane into 1 KB of LDS at the wave-uniform byte address in M0 (lane l
+// at +16 l).  It is written in asm so that the compiler, which cannot see
+// which LDS bytes such a load writes, does not wait for every one of them
+// before each LDS read; the kernel waits for them itself (tile_dma_wait)
+// before the barrier that publishes the tile.  The load has no result
+// register, and its address registers are read when it issues.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory");
+}
+// Wait until at most N of this wave's tile copies are still in flight
+// (vmcnt(N); the kernel has no other vector-memory loads in flight in its
+// loop, and copies complete in issue order).
+template <int N>
+__device__ __forceinline__ void tile_dma_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);  // vmcnt(N), expcnt(7), lgkmcnt(15)
+}
+
+// Tile copy: wave w's i-th piece is 1 KB of a slot (lane l at byte 16 l);
+// the lane fetches the logical chunk stored there.
 template <int D>
 struct Stager {
   uint32_t goff[Tile<D>::LOADS];   // byte offset in HBM from the tile's first row
-  uint32_t loff[Tile<D>::LOADS];   // byte offset in LDS of the piece in slot 0
+  uint32_t lblk[Tile<D>::LOADS];   // LDS byte offset of the wave's 1 KB block in slot 0 (wave-uniform)
 };
 
 template <int D>
@@ -103,18 +132,18 @@ __device__ __forceinline__ void make_stager(Stager<D>& sg, int64_t kv_ss, int wa
     int mat, r, c, P;
     T::piece(wave, lane, i, mat, r, c, P);
     sg.goff[i] = (uint32_t)(r * kv_ss * 2 + 16 * c);
-    sg.loff[i] = (mat ? T::V_REGION : 0) + 16 * P;
+    const int g = wave * T::LOADS + i;
+    sg.lblk[i] = (uint32_t)((mat ? T::V_REGION : 0) + 1024 * (g % T::PIECES));
   }
 }
 
-// HBM -> registers for tile [j0, j0+64).  Rows past kmax (only in a
-// workgroup's last tile) are clamped to kmax: their keys are masked and their
-// probabilities are 0, so the clamped (finite, written) rows never reach a
-// result and no unwritten cache slot is read.
-template <int D>
-__device__ __forceinline__ void fetch_tile(u32x4 (&st)[Tile<D>::LOADS], const Stager<D>& sg, const char* kb,
-                                           const char* vb, int64_t kv_ss, int j0, int kmax, int wave,
-                                           int lane) {
+// Copy tile [j0, j0+64) into ring slot SLOT.  Rows past kmax (only in a
+// workgroup's last tile) are clamped to kmax: their keys are masked and
+// their probabilities are 0, so the clamped (finite, written) rows never
+// reach a result and no unwritten cache slot is read.
+template <int D, int SLOT>
+__device__ __forceinline__ void dma_tile(const Stager<D>& sg, uint32_t lds0, const char* kb, const char* vb,
+                                         int64_t kv_ss, int j0, int kmax, int wave, int lane) {
   using T = Tile<D>;
   if (j0 + kKT - 1 <= kmax) {
     const char* kt = kb + (int64_t)j0 * kv_ss * 2;
@@ -122,7 +151,7 @@ __device__ __forceinline__ void fetch_tile(u32x4 (&st)[Tile<D>::LOADS], const St
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int mat = (wave * T::LOADS + i) / T::PIECES;
-      st[i] = ld16((mat ? vt : kt) + sg.goff[i]);
+      dma16((mat ? vt : kt) + sg.goff[i], lds0 + SLOT * T::MAT_BYTES + sg.lblk[i]);
     }
   } else {
 #pragma unroll
@@ -130,17 +159,19 @@ __device__ __forceinline__ void fetch_tile(u32x4 (&st)[Tile<D>::LOADS], const St
       int mat, r, c, P;
       T::piece(wave, lane, i, mat, r, c, P);
       const int key = min(j0 + r, kmax);
-      st[i] = ld16((mat ? vb : kb) + (int64_t)key * kv_ss * 2 + 16 * c);
+      dma16((mat ? vb : kb) + (int64_t)key * kv_ss * 2 + 16 * c, lds0 + SLOT * T::MAT_BYTES + sg.lblk[i]);
     }
   }
 }
 
-template <int D, int SLOT>
-__device__ __forceinline__ void store_tile(const u32x4 (&st)[Tile<D>::LOADS], const Stager<D>& sg, char* lds) {
-  using T = Tile<D>;
-#pragma unroll
-  for (int i = 0; i < T::LOADS; ++i)
-    *reinterpret_cast<u32x4*>(lds + sg.loff[i] + SLOT * T::MAT_BYTES) = st[i];
+// A workgroup barrier that waits for this wave's LDS accesses only: the
+// tile loads in flight to registers cross it.  The empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int D>
@@ -149,44 +180,84 @@ struct WaveCtx {
   const char* kp[D / 16];    // K-fragment address in slot 0, per k-step
   const char* vp[D / 32];    // V^T-fragment address in slot 0, per d-block
   f32x16 acc_o[D / 32];
+  f32x16 s[2];               // S^T of the tile between its matrix and vector phases
+  u32x4 pf[4];               // P^T (bf16) of the tile between its vector and matrix phases
   float m_run, l_run;
   float c;                   // scale * log2(e)
-  int mask_base;             // qabs - 4*half: key offset limit is mask_base - j0
+  int mask_base;             // first + pos(column) - 4*half: key offset limit is mask_base - j0
 };
 
-// Scores, online softmax and O update for the tile in slot SLOT.
-template <int D, int SLOT, bool MASK>
-__device__ __forceinline__ void compute_tile(WaveCtx<D>& w, int j0) {
+// Matrix phase: O^T += V^T P^T for the tile in slot SV (if PV), then
+// S^T = K Q^T for the tile in slot SK (if S).  S^T block kb holds keys
+// 32kb + 8(r/4) + 4half + r%4 of register r.  The 32 MFMAs run in chunks of
+// four, each chunk's LDS fragments read one chunk ahead (two chunks of
+// fragments live at a time, so the phase fits beside the wave's other
+// state); the S chunks alternate the two key blocks so that neighbouring
+// MFMAs are independent.
+template <int D, int SK, int SV, bool PV, bool S>
+__device__ __forceinline__ void mfma_phase(WaveCtx<D>& w) {
   using T = Tile<D>;
   constexpr int KS = T::KS, DB = T::DB;
-  // ---- S^T = K Q^T: block kb holds keys 32kb + 8(r/4) + 4half + r%4 ----
-  f32x16 s[2];
+  static_assert(DB <= 4, "one V^T fragment per d-block per chunk");
+  constexpr int NPV = PV ? 4 : 0;        // PV chunks: kk = 0..3, DB fragments each
+  constexpr int NS = S ? KS / 2 : 0;     // S chunks: k-steps 2c, 2c+1 of both key blocks
+  constexpr int N = NPV + NS;
+  if (S) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    u32x4 kf[KS];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = *reinterpret_cast<const u32x4*>(w.kp[ks] + SLOT * T::MAT_BYTES + kb * 32 * T::ROW_BYTES);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s[kb] = mfma(kf[ks], w.qf[ks], s[kb]);
+      for (int r = 0; r < 16; ++r) w.s[kb][r] = 0.f;
   }
-  // ---- causal mask (diagonal tiles only) ----
-  if (MASK) {
+  auto load = [&](int c, u32x4 (&f)[4]) {
+    if (c < NPV) {
+#pragma unroll
+      for (int q = 0; q < DB; ++q) f[q] = vt_frag<T::ROW_BYTES>(w.vp[q] + SV * T::MAT_BYTES + c * 16 * T::ROW_BYTES);
+    } else {
+      const int ks = 2 * (c - NPV);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f[i] = *reinterpret_cast<const u32x4*>(w.kp[ks + (i >> 1)] + SK * T::MAT_BYTES + (i & 1) * 32 * T::ROW_BYTES);
+    }
+  };
+  auto mma = [&](int c, const u32x4 (&f)[4]) {
+    if (c < NPV) {
+#pragma unroll
+      for (int q = 0; q < DB; ++q) w.acc_o[q] = mfma(f[q], w.pf[c], w.acc_o[q]);
+    } else {
+      const int ks = 2 * (c - NPV);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w.s[i & 1] = mfma(f[i], w.qf[ks + (i >> 1)], w.s[i & 1]);
+    }
+  };
+  if (N == 0) return;
+  u32x4 f0[4], f1[4];
+  load(0, f0);
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    if (c + 1 < N) load(c + 1, (c & 1) ? f0 : f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(c, (c & 1) ? f1 : f0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Vector phase of the tile starting at key j0: mask (diagonal tiles),
+// online softmax (log2 domain), P^T rounded to bf16 into w.pf.
+template <int D>
+__device__ __forceinline__ void softmax_phase(WaveCtx<D>& w, int j0, bool mask) {
+  constexpr int DB = Tile<D>::DB;
+  if (mask) {  // wave-uniform: diagonal tiles only
     const int lim = w.mask_base - j0;  // keep key offsets <= lim
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) w.s[kb][r] = -INFINITY;
   }
-  // ---- online softmax (log2 domain) ----
   // p = 2^(s*c - m) with the running max m, rounded to bf16 for the PV
   // product; the row sum adds the same rounded values (packed bf16 dot
   // products with 1.0), so the numerator and the denominator use identical
   // weights.
-  u32x4 pf[4];
   float ps;
   constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1.0, 1.0)
   auto probs = [&]() {
@@ -195,11 +266,11 @@ __device__ __forceinline__ void compute_tile(WaveCtx<D>& w, int j0) {
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e], w.c, -w.m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kk >> 1][8 * (kk & 1) + 2 * e + 1], w.c, -w.m_run));
-        pf[kk][e] = pack_bf16x2(p0, p1);
-        if (e & 1) ps1 = dot2_bf16(pf[kk][e], kOnes, ps1);
-        else ps0 = dot2_bf16(pf[kk][e], kOnes, ps0);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(w.s[kk >> 1][8 * (kk & 1) + 2 * e], w.c, -w.m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(w.s[kk >> 1][8 * (kk & 1) + 2 * e + 1], w.c, -w.m_run));
+        w.pf[kk][e] = pack_bf16x2(p0, p1);
+        if (e & 1) ps1 = dot2_bf16(w.pf[kk][e], kOnes, ps1);
+        else ps0 = dot2_bf16(w.pf[kk][e], kOnes, ps0);
       }
     }
     ps = ps0 + ps1;
@@ -208,19 +279,19 @@ __device__ __forceinline__ void compute_tile(WaveCtx<D>& w, int j0) {
   // The running max is raised (and O rescaled) only when the tile's max
   // exceeds it by more than the threshold, i.e. only if some p > 2^8 -- and
   // then the lane's sum of p exceeds 2^8 as well.  So the tile max is taken
-  // only on tiles where some lane's sum does (a row block's first tile, where
+  // only on tiles where some lane's sum does (a wave's first tile, where
   // m = -inf gives p = inf; a new max past the threshold; overflow): a rare,
   // wave-uniform branch that raises m, rescales and recomputes p.
   if (__builtin_amdgcn_ballot_w64(!(ps <= kSumTrigger))) {
-    float m0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-    float m1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+    float m0 = fmaxf(fmaxf(w.s[0][0], w.s[0][1]), w.s[0][2]);
+    float m1 = fmaxf(fmaxf(w.s[1][0], w.s[1][1]), w.s[1][2]);
 #pragma unroll
     for (int r = 3; r < 15; r += 2) {
-      m0 = fmaxf(fmaxf(m0, s[0][r]), s[0][r + 1]);
-      m1 = fmaxf(fmaxf(m1, s[1][r]), s[1][r + 1]);
+      m0 = fmaxf(fmaxf(m0, w.s[0][r]), w.s[0][r + 1]);
+      m1 = fmaxf(fmaxf(m1, w.s[1][r]), w.s[1][r + 1]);
     }
-    m0 = fmaxf(fmaxf(m0, s[0][15]), m1);
-    m0 = fmaxf(m0, s[1][15]);
+    m0 = fmaxf(fmaxf(m0, w.s[0][15]), m1);
+    m0 = fmaxf(m0, w.s[1][15]);
     const float tmax = max_halves(m0) * w.c;
     const float m_new = tmax > w.m_run + kRescaleThreshold ? tmax : w.m_run;
     float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);  // 0 on the first tile
@@ -236,71 +307,98 @@ __device__ __forceinline__ void compute_tile(WaveCtx<D>& w, int j0) {
     probs();
   }
   w.l_run += ps;
-  // ---- O^T += V^T P^T ----
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-    for (int q = 0; q < DB; ++q)
-      w.acc_o[q] = mfma(vt_frag<T::ROW_BYTES>(w.vp[q] + SLOT * T::MAT_BYTES + kk * 16 * T::ROW_BYTES), pf[kk], w.acc_o[q]);
 }
 
-// One step of the ring for tile jt in slot SLOT: fetch tile jt+2, multiply
-// tile jt, store tile jt+2 into the slot tile jt-2 used, and on odd steps
-// wait for every wave.  A store into tile jt-2's slot follows the barrier of
-// step jt-1 or jt-2, so every wave has finished that tile; a tile stored in
-// step jt is read in step jt+2, after the barrier of step jt or jt+1.
+// Per-wave bounds of the tile loop (wave-uniform).
+struct WaveTiles {
+  int last;       // last tile with a key of this wave (-1: no rows)
+  int diag_from;  // first tile that needs the causal mask
+};
+
+// The wave's program: for each tile k its matrix phase (tile k-1's PV and
+// tile k's S) then its vector phase (tile k's softmax), with a barrier
+// after each.  Both groups run this one program, group B (waves 4-7) one
+// barrier behind group A (waves 0-3): between two barriers the A wave of a
+// SIMD runs a matrix phase while its B wave runs a vector phase, and the
+// other way round in the next interval.
+//
+// The ring: the matrix phase of tile t starts the wave's copy of tile t+3
+// into the slot tile t-2 used (its last readers, the matrix phases of tile
+// t-1 in both groups, are behind a barrier), and ends by waiting for its
+// copy of tile t+1 (started two matrix phases earlier); the barrier after
+// it publishes tile t+1, whose first reader is the matrix phase of tile
+// t+1 in group A, two barriers later.  A copy thus has five phases to land.
+// SLOT = k % kSlots.
 template <int D, int SLOT>
-__device__ __forceinline__ void ring_step(WaveCtx<D>& w, u32x4 (&st)[Tile<D>::LOADS], const Stager<D>& sg,
-                                          char* lds, const char* kb, const char* vb, int64_t kv_ss, int jt,
-                                          int nkt, int kmax, int wave_last, int diag_from, int wave, int lane) {
-  const bool refill = jt + 2 < nkt;
-  if (refill) fetch_tile<D>(st, sg, kb, vb, kv_ss, (jt + 2) * kKT, kmax, wave, lane);
-  if (jt <= wave_last) {
-    if (jt < diag_from) compute_tile<D, SLOT, false>(w, jt * kKT);
-    else compute_tile<D, SLOT, true>(w, jt * kKT);
+__device__ __forceinline__ void matrix_step(WaveCtx<D>& w, const Stager<D>& sg, uint32_t lds0, const char* kb,
+                                            const char* vb, int64_t kv_ss, int k, int nkt, int kmax,
+                                            const WaveTiles& wt, int wave, int lane) {
+  using T = Tile<D>;
+  constexpr int SPREV = (SLOT + kSlots - 1) % kSlots;
+  if (k + 3 < nkt) dma_tile<D, (SLOT + 3) % kSlots>(sg, lds0, kb, vb, kv_ss, (k + 3) * kKT, kmax, wave, lane);
+  // k < nkt here.  A wave past its last tile still forms S (discarded: no
+  // vector phase follows) in the step that adds its last PV, so the loop
+  // carries one form of the phase.
+  if (k == 0) {
+    if (wt.last >= 0) mfma_phase<D, SLOT, SPREV, false, true>(w);
+  } else if (k - 1 <= wt.last) {
+    mfma_phase<D, SLOT, SPREV, true, true>(w);
   }
-  if (refill) store_tile<D, (SLOT + 2) % kSlots>(st, sg, lds);
-  if (SLOT & 1) __syncthreads();
+  // tile k+1 landed: the copies of tiles k+2 and k+3 may still be in flight
+  if (k + 3 < nkt) tile_dma_wait<2 * T::LOADS>();
+  else if (k + 2 < nkt) tile_dma_wait<T::LOADS>();
+  else tile_dma_wait<0>();
+  phase_barrier();
+}
+
+template <int D>
+__device__ __forceinline__ void vector_step(WaveCtx<D>& w, int t, const WaveTiles& wt) {
+  if (t <= wt.last) softmax_phase<D>(w, t * kKT, t >= wt.diag_from);
+  phase_barrier();
+}
+
+template <int D, int SLOT>
+__device__ __forceinline__ void tile_step(WaveCtx<D>& w, const Stager<D>& sg, uint32_t lds0, const char* kb,
+                                          const char* vb, int64_t kv_ss, int k, int nkt, int kmax,
+                                          const WaveTiles& wt, int wave, int lane) {
+  matrix_step<D, SLOT>(w, sg, lds0, kb, vb, kv_ss, k, nkt, kmax, wt, wave, lane);
+  vector_step<D>(w, k, wt);
 }
 
 // D: head dim (32, 64 or 128).
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int nqt) {
+__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int nrb) {
   using T = Tile<D>;
   constexpr int KS = T::KS, DB = T::DB;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   // XCD-aware order.  Workgroup i runs on XCD i % 8.  Units u = (sequence,
-  // KV head) stay on one XCD, so the query heads of a unit share its K/V in
+  // KV head) stay on one XCD, so the row blocks of a unit share its K/V in
   // that XCD's L2 (and the MALL behind it).  XCD x takes the units u = x
-  // (mod 8) in groups of four and walks each group q-tile slab by slab,
-  // heaviest slab first, so heavy tiles start early and light ones fill the
-  // end.  Walking unit by unit (heaviest tile first within each unit) leaves
-  // heavy tiles of the last units for the end: on the 3.8B-shaped batch the
-  // busiest compute unit then carries 120 tile-steps against an average of
-  // 108 (112 with groups of four).  Larger groups balance a little better
-  // but spread a unit's q-tiles over more time, so its K/V tiles are
-  // fetched again; packed documents, whose lengths differ widely, use one
-  // group (all their units) so the long documents' heavy tiles start at once.
+  // (mod 8) in groups of four and walks each group row block by row block,
+  // heaviest (last) block first, so heavy blocks start early and light ones
+  // fill the end.  Packed documents, whose lengths differ widely, use one
+  // group (all their units) so the long documents' heavy blocks start at
+  // once.
   const int group = p.Hq / p.Hkv;
-  int qt, b, kvh, h;
+  int rb, b, kvh;
   {
     const int units = p.B * p.Hkv;
     const int x = (int)(blockIdx.x % kXcds), r = (int)(blockIdx.x / kXcds);
     const int cnt = x < units ? (units - x + kXcds - 1) / kXcds : 0;  // units u = x (mod 8)
-    if (r >= cnt * group * nqt) return;
-    const int G = p.cu_seqlens ? cnt : 4;  // units walked together, slab by slab
-    const int gi = r / (G * group * nqt), g0 = gi * G, gn = min(G, cnt - g0);
-    const int rr = r - gi * G * group * nqt;
-    const int per_slab = gn * group;
-    const int within = rr % per_slab;
-    qt = nqt - 1 - rr / per_slab;
-    const int u = x + kXcds * (g0 + within / group);
+    if (r >= cnt * nrb) return;
+    const int G = p.cu_seqlens ? cnt : 4;  // units walked together, block by block
+    const int gi = r / (G * nrb), g0 = gi * G, gn = min(G, cnt - g0);
+    const int rr = r - gi * G * nrb;
+    rb = nrb - 1 - rr / gn;
+    const int u = x + kXcds * (g0 + rr % gn);
     kvh = u % p.Hkv;
     b = u / p.Hkv;
-    h = kvh * group + within % group;
   }
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // The wave index is wave-uniform; through readfirstlane the compiler
+  // knows it, so the group's branches around the barriers are scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   // Rows of this sequence.  Padded batch: row s of sequence b sits at slot
@@ -317,29 +415,38 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
       if (tid == 0 && p.err) p.err[0] = 1;
       return;
     }
-    if (qt * kBM >= Sq) return;  // past this document's rows
   }
-  const int s_base = qt * kBM + wave * 32;  // this wave's first row
-  const int64_t q_row0 = (int64_t)b * p.q_sb + tok0 * p.q_ss + (int64_t)h * p.q_sh;
-  const int64_t o_row0 = (int64_t)b * p.o_sb + tok0 * p.o_ss + (int64_t)h * p.o_sh;
-  const int64_t lse_row0 = p.cu_seqlens ? (int64_t)h * p.S_max + tok0 : ((int64_t)b * p.Hq + h) * Sq;
+  const int nrows = Sq * group;                // (position, head) rows of this unit
+  const int R0 = rb * kRows;
+  if (R0 >= nrows) return;                     // past this document's rows (whole workgroup)
+  // This lane's column: row R = pos * group + head.
+  const int R = R0 + wave * 32 + col;
+  const int pos = R / group, h = kvh * group + R % group;
+  const bool col_ok = R < nrows;
+  const int64_t lse_base = p.cu_seqlens ? (int64_t)h * p.S_max + tok0 : ((int64_t)b * p.Hq + h) * Sq;
   if (first < 0 || (int64_t)first + Sq > p.S_max) {
     // Device-side capacity violation: NaN rows, flag, no cache access.
-    if (s_base + col < Sq && half == 0) {
-      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + o_row0 + (int64_t)(s_base + col) * p.o_ss;
+    if (col_ok && half == 0) {
+      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (tok0 + pos) * p.o_ss +
+                     (int64_t)h * p.o_sh;
       for (int d = 0; d < D; ++d) orow[d] = 0x7FC0;
-      if (p.lse) p.lse[lse_row0 + s_base + col] = __builtin_nanf("");
+      if (p.lse) p.lse[lse_base + pos] = __builtin_nanf("");
     }
     if (tid == 0 && p.err) p.err[0] = 1;
     return;
   }
 
-  const int s_end_wg = min(Sq, (qt + 1) * kBM);       // rows [qt*kBM, s_end_wg)
-  const int kmax = first + s_end_wg - 1;                // last key the workgroup needs
+  // Tiles of the workgroup and of this wave (wave-uniform).
+  const int pos_hi_wg = min(Sq - 1, (min(nrows, R0 + kRows) - 1) / group);
+  const int kmax = first + pos_hi_wg;  // last key the workgroup needs
   const int nkt = kmax / kKT + 1;
-  const int wave_rows = min(32, Sq - s_base);           // <= 0: a wave past the ragged tail
-  const int wave_last = wave_rows > 0 ? (first + s_base + wave_rows - 1) / kKT : -1;
-  const int diag_from = (first + s_base) / kKT;         // first tile that needs the mask
+  WaveTiles wt;
+  {
+    const int wr0 = R0 + wave * 32;
+    const int wr1 = min(nrows, wr0 + 32) - 1;  // < wr0: a wave past the rows
+    wt.last = wr1 >= wr0 ? (first + wr1 / group) / kKT : -1;
+    wt.diag_from = (first + wr0 / group) / kKT;
+  }
 
   const int64_t kv_off = ((int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh + tok0 * p.kv_ss) * 2;
   const char* kb = reinterpret_cast<const char*>(p.k) + kv_off;
@@ -347,14 +454,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
 
   WaveCtx<D> w;
   w.c = p.scale * kLog2e;
-  w.mask_base = first + s_base + col - 4 * half;
+  w.mask_base = first + pos - 4 * half;
   {
-    // Q^T fragments: lane holds query `col`, d = 16*ks + 8*half .. +8.
-    const int s = s_base + col;
-    const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + q_row0 + (int64_t)s * p.q_ss;
+    // Q^T fragments: lane holds column `col`, d = 16*ks + 8*half .. +8.
+    const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * p.q_sb + (tok0 + pos) * p.q_ss +
+                       (int64_t)h * p.q_sh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      w.qf[ks] = (s < Sq) ? ld16(qr + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < KS; ++ks) w.qf[ks] = col_ok ? ld16(qr + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
+    // Q lands before the tile copies are issued, so the first use of Q
+    // does not wait for them.
+    tile_dma_wait<0>();
   }
   // K fragment: row `col` (block 1 is 32 rows further) at logical chunk
   // 2ks + half.  V^T fragment for d-block q: rows 4half + x/4 (+16kk, +8),
@@ -379,35 +488,59 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
 
   Stager<D> sg;
   make_stager<D>(sg, p.kv_ss, wave, lane);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;  // LDS byte address of the ring
 
-  // Prologue: tiles 0 and 1 into slots 0 and 1.
-  u32x4 st[T::LOADS];
-  fetch_tile<D>(st, sg, kb, vb, p.kv_ss, 0, kmax, wave, lane);
-  store_tile<D, 0>(st, sg, lds);
-  if (nkt > 1) {
-    fetch_tile<D>(st, sg, kb, vb, p.kv_ss, kKT, kmax, wave, lane);
-    store_tile<D, 1>(st, sg, lds);
+  // Prologue: tiles 0, 1 and 2 into slots 0, 1 and 2; tiles 0 and 1 must
+  // have landed before the first matrix phase, tile 2 before the second.
+  dma_tile<D, 0>(sg, lds0, kb, vb, p.kv_ss, 0, kmax, wave, lane);
+  if (nkt > 1) dma_tile<D, 1>(sg, lds0, kb, vb, p.kv_ss, kKT, kmax, wave, lane);
+  if (nkt > 2) {
+    dma_tile<D, 2>(sg, lds0, kb, vb, p.kv_ss, 2 * kKT, kmax, wave, lane);
+    tile_dma_wait<T::LOADS>();
+  } else {
+    tile_dma_wait<0>();
   }
-  __syncthreads();
+  phase_barrier();
 
-  for (int jt = 0; jt < nkt; jt += kSlots) {
-    ring_step<D, 0>(w, st, sg, lds, kb, vb, p.kv_ss, jt, nkt, kmax, wave_last, diag_from, wave, lane);
-    if (jt + 1 >= nkt) break;
-    ring_step<D, 1>(w, st, sg, lds, kb, vb, p.kv_ss, jt + 1, nkt, kmax, wave_last, diag_from, wave, lane);
-    if (jt + 2 >= nkt) break;
-    ring_step<D, 2>(w, st, sg, lds, kb, vb, p.kv_ss, jt + 2, nkt, kmax, wave_last, diag_from, wave, lane);
-    if (jt + 3 >= nkt) break;
-    ring_step<D, 3>(w, st, sg, lds, kb, vb, p.kv_ss, jt + 3, nkt, kmax, wave_last, diag_from, wave, lane);
+  // Group B starts one barrier late and group A ends with one more, so
+  // every wave passes the same barriers.
+  const bool group_b = wave >= kWaves / 2;
+  if (group_b) phase_barrier();
+  // tile 0: S only
+  matrix_step<D, 0>(w, sg, lds0, kb, vb, p.kv_ss, 0, nkt, kmax, wt, wave, lane);
+  vector_step<D>(w, 0, wt);
+  for (int k = 1; k < nkt; k += kSlots) {
+    tile_step<D, 1>(w, sg, lds0, kb, vb, p.kv_ss, k, nkt, kmax, wt, wave, lane);
+    if (k + 1 >= nkt) break;
+    tile_step<D, 2>(w, sg, lds0, kb, vb, p.kv_ss, k + 1, nkt, kmax, wt, wave, lane);
+    if (k + 2 >= nkt) break;
+    tile_step<D, 3>(w, sg, lds0, kb, vb, p.kv_ss, k + 2, nkt, kmax, wt, wave, lane);
+    if (k + 3 >= nkt) break;
+    tile_step<D, 4>(w, sg, lds0, kb, vb, p.kv_ss, k + 3, nkt, kmax, wt, wave, lane);
+    if (k + 4 >= nkt) break;
+    tile_step<D, 0>(w, sg, lds0, kb, vb, p.kv_ss, k + 4, nkt, kmax, wt, wave, lane);
   }
+  // the last tile's PV (slot (nkt - 1) % kSlots)
+  if (nkt - 1 <= wt.last) {
+    switch ((nkt - 1) % kSlots) {
+      case 0: mfma_phase<D, 0, 0, true, false>(w); break;
+      case 1: mfma_phase<D, 0, 1, true, false>(w); break;
+      case 2: mfma_phase<D, 0, 2, true, false>(w); break;
+      case 3: mfma_phase<D, 0, 3, true, false>(w); break;
+      default: mfma_phase<D, 0, 4, true, false>(w); break;
+    }
+  }
+  phase_barrier();
+  if (!group_b) phase_barrier();
 
   // ---- epilogue: O = O^T / l, rounded to bf16 ----
-  // acc_o[q] register r holds d = 32q + 8(r/4) + 4half + r%4 of query col.
-  if (wave_last >= 0) {
+  // acc_o[q] register r holds d = 32q + 8(r/4) + 4half + r%4 of column col.
+  if (wt.last >= 0) {
     const float lsum = sum_halves(w.l_run);
-    const int s = s_base + col;
-    if (s < Sq) {
+    if (col_ok) {
       const float inv = 1.f / lsum;
-      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + o_row0 + (int64_t)s * p.o_ss;
+      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (tok0 + pos) * p.o_ss +
+                     (int64_t)h * p.o_sh;
 #pragma unroll
       for (int q = 0; q < DB; ++q)
 #pragma unroll
@@ -418,19 +551,20 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
           wv[1] = pack_bf16x2(w.acc_o[q][4 * q4 + 2] * inv, w.acc_o[q][4 * q4 + 3] * inv);
           *reinterpret_cast<u32x2*>(orow + d) = wv;
         }
-      if (p.lse && half == 0) p.lse[lse_row0 + s] = (w.m_run + log2f(lsum)) * kLn2;
+      if (p.lse && half == 0) p.lse[lse_base + pos] = (w.m_run + log2f(lsum)) * kLn2;
     }
   }
 }
 
 template <int D>
 hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
-  const int nqt = (p.Sq + kBM - 1) / kBM;
+  const int group = p.Hq / p.Hkv;
+  const int nrb = (int)(((int64_t)p.Sq * group + kRows - 1) / kRows);
   // every XCD sized for the largest unit share
-  const int64_t total = (int64_t)kXcds * ((p.B * p.Hkv + kXcds - 1) / kXcds) * (p.Hq / p.Hkv) * nqt;
-  const dim3 grid((unsigned)(((total + kXcds - 1) / kXcds) * kXcds));
+  const int64_t total = (int64_t)kXcds * ((p.B * p.Hkv + kXcds - 1) / kXcds) * nrb;
   KernelTimer kt_("prefill_kernel", stream);
-  hipLaunchKernelGGL(prefill_kernel<D>, grid, dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream, p, nqt);
+  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)total), dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream,
+                     p, nrb);
   return hipGetLastError();
 }
 
