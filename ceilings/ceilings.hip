@@ -11,6 +11,12 @@
 //    v_mfma_f32_32x32x16_bf16 on four independent accumulators (no memory
 //    traffic in the loop).  flops / time is the matrix-core rate a kernel
 //    can reach at the clock the chip holds under that load.
+//  * ceil_lds_mfma: workgroups of 8 waves (two per SIMD) on a 64 KiB LDS
+//    image.  mode 0 reads 16 bytes per lane per instruction and folds them
+//    (LDS read bandwidth alone); mode 1 feeds every 32 x 32 x 16 matrix
+//    instruction a B operand of 16 bytes per lane read from LDS just before
+//    it, the operand traffic of a kernel whose waves each read a whole
+//    shared K or V tile.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -79,6 +85,44 @@ __global__ void __launch_bounds__(256) mfma_bf16_kernel(float* __restrict__ out,
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// One 16-byte piece per lane, consecutive lanes on consecutive pieces (no
+// bank conflict), the wave's 1 KiB block moving by one block per read.
+template <bool MFMA>
+__global__ void __launch_bounds__(512) lds_mfma_kernel(float* __restrict__ out, int iters) {
+  __shared__ u32x4 img[4096];
+  const uint32_t t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (uint32_t i = t; i < 4096; i += 512) img[i] = u32x4{i, i * 3u + 1u, i ^ 0x3F80u, 0x3F803F80u};
+  __syncthreads();
+  u32x4 av = {0x3F803F80u ^ t, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  uint32_t acc = 0;
+  uint32_t blk = wave * 8;
+  // Software-pipelined: the four operands of the next step are read while
+  // this step's instructions run.
+  u32x4 b0 = img[(blk & 63) * 64 + lane], b1 = img[((blk + 1) & 63) * 64 + lane];
+  u32x4 b2 = img[((blk + 2) & 63) * 64 + lane], b3 = img[((blk + 3) & 63) * 64 + lane];
+  for (int i = 0; i < iters; ++i) {
+    blk += 4;
+    const u32x4 n0 = img[(blk & 63) * 64 + lane], n1 = img[((blk + 1) & 63) * 64 + lane];
+    const u32x4 n2 = img[((blk + 2) & 63) * 64 + lane], n3 = img[((blk + 3) & 63) * 64 + lane];
+    if (MFMA) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, b0), c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, b1), c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, b2), c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, b3), c3, 0, 0, 0);
+    } else {
+      acc ^= fold(b0) ^ fold(b1) ^ fold(b2) ^ fold(b3);
+    }
+    b0 = n0; b1 = n1; b2 = n2; b3 = n3;
+  }
+  acc ^= fold(b0) ^ fold(b1) ^ fold(b2) ^ fold(b3);
+  float s = (float)acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  out[(size_t)blockIdx.x * blockDim.x + t] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,6 +151,17 @@ int ceil_stream_read(const void* src, size_t bytes, uint32_t* out, int wgs, int 
 int ceil_mfma_bf16(float* out, int wgs, int iters, void* stream) {
   if (!out || wgs <= 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(mfma_bf16_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : -9;
+}
+
+// `wgs` workgroups of 8 waves, each wave `iters` x 4 LDS reads of 16 bytes
+// per lane (1 KiB per wave per read), with (mode 1) or without (mode 0) a
+// 32 x 32 x 16 matrix instruction consuming each; out receives wgs * 512
+// floats.
+int ceil_lds_mfma(float* out, int wgs, int iters, int mode, void* stream) {
+  if (!out || wgs <= 0 || iters <= 0 || mode < 0 || mode > 1) return -1;
+  if (mode) hipLaunchKernelGGL(lds_mfma_kernel<true>, dim3(wgs), dim3(512), 0, (hipStream_t)stream, out, iters);
+  else hipLaunchKernelGGL(lds_mfma_kernel<false>, dim3(wgs), dim3(512), 0, (hipStream_t)stream, out, iters);
   return hipGetLastError() == hipSuccess ? 0 : -9;
 }
 

@@ -44,9 +44,11 @@
 //  * the causal mask is applied on diagonal tiles only; tiles past a wave's
 //    last row are skipped (the wave still keeps the barriers); workgroups
 //    are issued heaviest row block first, XCD-aware.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
+
 #include "launch.h"
 #include "mfma_attn.h"
 
@@ -103,8 +105,22 @@ struct Tile {
 // before each LDS read; the kernel waits for them itself (tile_dma_wait)
 // before the barrier that publishes the tile.  The load has no result
 // register, and its address registers are read when it issues.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+//
+// dma16 addresses HBM as a scalar base plus a per-lane 32-bit offset and
+// LDS as a scalar base plus the constant IMM, both sums formed inside the
+// asm: the copy costs no vector instruction (which would queue behind the
+// other wave's softmax) and the compiler keeps no per-copy address live.
+template <int IMM>
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase),
+               "s"(lds_base), "i"(IMM)
+               : "memory");
+}
+// The general form: a per-lane 64-bit address.
+template <int IMM>
+__device__ __forceinline__ void dma16_v(const void* g, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base),
+               "i"(IMM)
                : "memory");
 }
 // Wait until at most N of this wave's tile copies are still in flight
@@ -120,21 +136,27 @@ __device__ __forceinline__ void tile_dma_wait() {
 // the lane fetches the logical chunk stored there.
 template <int D>
 struct Stager {
-  uint32_t goff[Tile<D>::LOADS];   // byte offset in HBM from the tile's first row
-  uint32_t lblk[Tile<D>::LOADS];   // LDS byte offset of the wave's 1 KB block in slot 0 (wave-uniform)
+  uint32_t goff[Tile<D>::LOADS];  // byte offset in HBM from the tile's first row
+  uint32_t lblk;                  // LDS byte offset of the wave's first 1 KB block in slot 0 (wave-uniform)
+  bool v;                         // the wave copies V (else K) (wave-uniform)
 };
 
+// A wave's LOADS pieces are consecutive 1 KB blocks of one matrix (PIECES is
+// a multiple of LOADS), so one base and constant steps address them.
 template <int D>
 __device__ __forceinline__ void make_stager(Stager<D>& sg, int64_t kv_ss, int wave, int lane) {
   using T = Tile<D>;
+  static_assert(T::PIECES % T::LOADS == 0, "a wave's pieces stay in one matrix");
+  static_assert(T::LOADS >= 1 && T::LOADS <= 4, "dma_tile issues up to four copies");
 #pragma unroll
   for (int i = 0; i < T::LOADS; ++i) {
     int mat, r, c, P;
     T::piece(wave, lane, i, mat, r, c, P);
     sg.goff[i] = (uint32_t)(r * kv_ss * 2 + 16 * c);
-    const int g = wave * T::LOADS + i;
-    sg.lblk[i] = (uint32_t)((mat ? T::V_REGION : 0) + 1024 * (g % T::PIECES));
   }
+  const int g = wave * T::LOADS;
+  sg.v = g >= T::PIECES;
+  sg.lblk = (uint32_t)((sg.v ? T::V_REGION : 0) + 1024 * (g % T::PIECES));
 }
 
 // Copy tile [j0, j0+64) into ring slot SLOT.  Rows past kmax (only in a
@@ -145,22 +167,26 @@ template <int D, int SLOT>
 __device__ __forceinline__ void dma_tile(const Stager<D>& sg, uint32_t lds0, const char* kb, const char* vb,
                                          int64_t kv_ss, int j0, int kmax, int wave, int lane) {
   using T = Tile<D>;
+  const uint32_t lb = lds0 + sg.lblk;
   if (j0 + kKT - 1 <= kmax) {
-    const char* kt = kb + (int64_t)j0 * kv_ss * 2;
-    const char* vt = vb + (int64_t)j0 * kv_ss * 2;
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      const int mat = (wave * T::LOADS + i) / T::PIECES;
-      dma16((mat ? vt : kt) + sg.goff[i], lds0 + SLOT * T::MAT_BYTES + sg.lblk[i]);
-    }
+    const char* base = (sg.v ? vb : kb) + (int64_t)j0 * kv_ss * 2;
+    dma16<SLOT * T::MAT_BYTES>(base, sg.goff[0], lb);
+    if constexpr (T::LOADS > 1) dma16<SLOT * T::MAT_BYTES + 1024>(base, sg.goff[1], lb);
+    if constexpr (T::LOADS > 2) dma16<SLOT * T::MAT_BYTES + 2048>(base, sg.goff[2], lb);
+    if constexpr (T::LOADS > 3) dma16<SLOT * T::MAT_BYTES + 3072>(base, sg.goff[3], lb);
   } else {
+    int key[T::LOADS], c[T::LOADS];
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      int mat, r, c, P;
-      T::piece(wave, lane, i, mat, r, c, P);
-      const int key = min(j0 + r, kmax);
-      dma16((mat ? vb : kb) + (int64_t)key * kv_ss * 2 + 16 * c, lds0 + SLOT * T::MAT_BYTES + sg.lblk[i]);
+      int mat, r, P;
+      T::piece(wave, lane, i, mat, r, c[i], P);
+      key[i] = min(j0 + r, kmax);
     }
+    const char* base = sg.v ? vb : kb;
+    dma16_v<SLOT * T::MAT_BYTES>(base + (int64_t)key[0] * kv_ss * 2 + 16 * c[0], lb);
+    if constexpr (T::LOADS > 1) dma16_v<SLOT * T::MAT_BYTES + 1024>(base + (int64_t)key[1] * kv_ss * 2 + 16 * c[1], lb);
+    if constexpr (T::LOADS > 2) dma16_v<SLOT * T::MAT_BYTES + 2048>(base + (int64_t)key[2] * kv_ss * 2 + 16 * c[2], lb);
+    if constexpr (T::LOADS > 3) dma16_v<SLOT * T::MAT_BYTES + 3072>(base + (int64_t)key[3] * kv_ss * 2 + 16 * c[3], lb);
   }
 }
 
@@ -247,33 +273,49 @@ template <int D>
 __device__ __forceinline__ void softmax_phase(WaveCtx<D>& w, int j0, bool mask) {
   constexpr int DB = Tile<D>::DB;
   if (mask) {  // wave-uniform: diagonal tiles only
-    const int lim = w.mask_base - j0;  // keep key offsets <= lim
+    // Keep key offsets <= lim.  Each score is clamped from above by +inf
+    // (kept) or -inf (masked): the bound's sign is the sign of lim - off.
+    // Integer and min instructions only, so no per-element comparison
+    // result occupies a scalar register pair.
+    const int lim = w.mask_base - j0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) w.s[kb][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int d = lim - (32 * kb + 8 * (r >> 2) + (r & 3));
+        const float bound = __builtin_bit_cast(float, ((uint32_t)d & 0x80000000u) | 0x7F800000u);
+        w.s[kb][r] = fminf(w.s[kb][r], bound);
+      }
   }
   // p = 2^(s*c - m) with the running max m, rounded to bf16 for the PV
-  // product; the row sum adds the same rounded values (packed bf16 dot
-  // products with 1.0), so the numerator and the denominator use identical
-  // weights.
+  // product; the row sum adds the same rounded values, so the numerator and
+  // the denominator use identical weights.  The rounded values are read
+  // back out of the packed pair (a bf16 is the top half of a float) and
+  // added in fp32: the packed bf16 dot instruction would do the same in one
+  // step, but it runs on the matrix pipeline and stalls the other wave's
+  // matrix instructions, while shifts, masks and adds issue beside them.
   float ps;
-  constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1.0, 1.0)
   auto probs = [&]() {
-    float ps0 = 0.f, ps1 = 0.f;
+    float ps0 = 0.f, ps1 = 0.f, ps2 = 0.f, ps3 = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(w.s[kk >> 1][8 * (kk & 1) + 2 * e], w.c, -w.m_run));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(w.s[kk >> 1][8 * (kk & 1) + 2 * e + 1], w.c, -w.m_run));
-        w.pf[kk][e] = pack_bf16x2(p0, p1);
-        if (e & 1) ps1 = dot2_bf16(w.pf[kk][e], kOnes, ps1);
-        else ps0 = dot2_bf16(w.pf[kk][e], kOnes, ps0);
+        const uint32_t pk = pack_bf16x2(p0, p1);
+        w.pf[kk][e] = pk;
+        const float r0 = __builtin_bit_cast(float, pk << 16), r1 = __builtin_bit_cast(float, pk & 0xffff0000u);
+        if (e & 1) {
+          ps2 += r0;
+          ps3 += r1;
+        } else {
+          ps0 += r0;
+          ps1 += r1;
+        }
       }
     }
-    ps = ps0 + ps1;
+    ps = (ps0 + ps1) + (ps2 + ps3);
   };
   probs();
   // The running max is raised (and O rescaled) only when the tile's max
@@ -365,40 +407,15 @@ __device__ __forceinline__ void tile_step(WaveCtx<D>& w, const Stager<D>& sg, ui
   vector_step<D>(w, k, wt);
 }
 
-// D: head dim (32, 64 or 128).
+// One work item: row block rb of unit (sequence b, KV head kvh).  Every
+// wave of the workgroup runs it and passes the same barriers, so items
+// chain in a persistent workgroup; an item that needs no work (rows past a
+// document's end, a capacity violation) is skipped by the whole workgroup.
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int nrb) {
+__device__ __forceinline__ void run_item(const AttnParams& p, char* lds, int group, int b, int kvh, int rb,
+                                         int tid, int lane, int wave) {
   using T = Tile<D>;
   constexpr int KS = T::KS, DB = T::DB;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-
-  // XCD-aware order.  Workgroup i runs on XCD i % 8.  Units u = (sequence,
-  // KV head) stay on one XCD, so the row blocks of a unit share its K/V in
-  // that XCD's L2 (and the MALL behind it).  XCD x takes the units u = x
-  // (mod 8) in groups of four and walks each group row block by row block,
-  // heaviest (last) block first, so heavy blocks start early and light ones
-  // fill the end.  Packed documents, whose lengths differ widely, use one
-  // group (all their units) so the long documents' heavy blocks start at
-  // once.
-  const int group = p.Hq / p.Hkv;
-  int rb, b, kvh;
-  {
-    const int units = p.B * p.Hkv;
-    const int x = (int)(blockIdx.x % kXcds), r = (int)(blockIdx.x / kXcds);
-    const int cnt = x < units ? (units - x + kXcds - 1) / kXcds : 0;  // units u = x (mod 8)
-    if (r >= cnt * nrb) return;
-    const int G = p.cu_seqlens ? cnt : 4;  // units walked together, block by block
-    const int gi = r / (G * nrb), g0 = gi * G, gn = min(G, cnt - g0);
-    const int rr = r - gi * G * nrb;
-    rb = nrb - 1 - rr / gn;
-    const int u = x + kXcds * (g0 + rr % gn);
-    kvh = u % p.Hkv;
-    b = u / p.Hkv;
-  }
-  const int tid = threadIdx.x, lane = tid & 63;
-  // The wave index is wave-uniform; through readfirstlane the compiler
-  // knows it, so the group's branches around the barriers are scalar.
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   // Rows of this sequence.  Padded batch: row s of sequence b sits at slot
@@ -452,6 +469,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
   const char* kb = reinterpret_cast<const char*>(p.k) + kv_off;
   const char* vb = reinterpret_cast<const char*>(p.v) + kv_off;
 
+  // Prologue: tiles 0, 1 and 2 into ring slots 0, 1 and 2, then this
+  // lane's Q, all in flight together; one wait covers them (the first use
+  // of Q then waits for nothing, as the loads it counts have landed).
+  Stager<D> sg;
+  make_stager<D>(sg, p.kv_ss, wave, lane);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;  // LDS byte address of the ring
+  dma_tile<D, 0>(sg, lds0, kb, vb, p.kv_ss, 0, kmax, wave, lane);
+  if (nkt > 1) dma_tile<D, 1>(sg, lds0, kb, vb, p.kv_ss, kKT, kmax, wave, lane);
+  if (nkt > 2) dma_tile<D, 2>(sg, lds0, kb, vb, p.kv_ss, 2 * kKT, kmax, wave, lane);
+
   WaveCtx<D> w;
   w.c = p.scale * kLog2e;
   w.mask_base = first + pos - 4 * half;
@@ -461,8 +488,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
                        (int64_t)h * p.q_sh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) w.qf[ks] = col_ok ? ld16(qr + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
-    // Q lands before the tile copies are issued, so the first use of Q
-    // does not wait for them.
     tile_dma_wait<0>();
   }
   // K fragment: row `col` (block 1 is 32 rows further) at logical chunk
@@ -486,20 +511,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
   w.m_run = -INFINITY;
   w.l_run = 0.f;
 
-  Stager<D> sg;
-  make_stager<D>(sg, p.kv_ss, wave, lane);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;  // LDS byte address of the ring
-
-  // Prologue: tiles 0, 1 and 2 into slots 0, 1 and 2; tiles 0 and 1 must
-  // have landed before the first matrix phase, tile 2 before the second.
-  dma_tile<D, 0>(sg, lds0, kb, vb, p.kv_ss, 0, kmax, wave, lane);
-  if (nkt > 1) dma_tile<D, 1>(sg, lds0, kb, vb, p.kv_ss, kKT, kmax, wave, lane);
-  if (nkt > 2) {
-    dma_tile<D, 2>(sg, lds0, kb, vb, p.kv_ss, 2 * kKT, kmax, wave, lane);
-    tile_dma_wait<T::LOADS>();
-  } else {
-    tile_dma_wait<0>();
-  }
   phase_barrier();
 
   // Group B starts one barrier late and group A ends with one more, so
@@ -556,15 +567,75 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
   }
 }
 
+// D: head dim (32, 64 or 128).
+//
+// Work order, XCD-aware.  Workgroup i runs on XCD i % 8.  Units u =
+// (sequence, KV head) stay on one XCD, so the row blocks of a unit share
+// its K/V in that XCD's L2 (and the MALL behind it).
+//  * One item per workgroup (persistent == 0): XCD x takes the units u = x
+//    (mod 8) in groups of four and walks each group row block by row block,
+//    heaviest (last) block first, so heavy blocks start early and light
+//    ones fill the end.  Packed documents, whose lengths differ widely, use
+//    one group (all their units) so the long documents' heavy blocks start
+//    at once.
+//  * Persistent (one workgroup per compute unit): XCD x's items, in the
+//    same order, are dealt to its workgroups in snake order (0..n-1,
+//    n-1..0, ...), which evens out the sums of their tile counts; the
+//    workgroups never leave the compute unit, so no item waits for a
+//    workgroup launch.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int nrb, int persistent) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int group = p.Hq / p.Hkv;
+  const int units = p.B * p.Hkv;
+  const int x = (int)(blockIdx.x % kXcds), r = (int)(blockIdx.x / kXcds);
+  const int cnt = x < units ? (units - x + kXcds - 1) / kXcds : 0;  // units u = x (mod 8)
+  const int tid = threadIdx.x, lane = tid & 63;
+  // The wave index is wave-uniform; through readfirstlane the compiler
+  // knows it, so the group's branches around the barriers are scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = (int)(gridDim.x / kXcds);
+  const int G = p.cu_seqlens ? cnt : 4;  // units walked together, block by block
+  for (int it = 0;; ++it) {
+    // k: this workgroup's it-th item in its XCD's list
+    const int k = persistent ? it * nw + ((it & 1) ? nw - 1 - r : r) : (it == 0 ? r : cnt * nrb);
+    if (k >= cnt * nrb) break;
+    const int gi = k / (G * nrb), g0 = gi * G, gn = min(G, cnt - g0);
+    const int kk = k - gi * G * nrb;
+    const int u = x + kXcds * (g0 + kk % gn);
+    run_item<D>(p, lds, group, u / p.Hkv, u % p.Hkv, nrb - 1 - kk / gn, tid, lane, wave);
+  }
+}
+
+// Compute units of the current device (cached per device).
+int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int D>
 hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   const int group = p.Hq / p.Hkv;
   const int nrb = (int)(((int64_t)p.Sq * group + kRows - 1) / kRows);
   // every XCD sized for the largest unit share
   const int64_t total = (int64_t)kXcds * ((p.B * p.Hkv + kXcds - 1) / kXcds) * nrb;
+  // More items than compute units (one workgroup fits a compute unit): one
+  // persistent workgroup per compute unit, a multiple of the XCD count so
+  // every XCD holds as many.  Packed documents keep one item per workgroup
+  // (their row counts are on the device only).
+  const int cus = compute_units() / kXcds * kXcds;
+  const bool persistent = !p.cu_seqlens && cus > 0 && total > cus;
+  const unsigned grid = persistent ? (unsigned)cus : (unsigned)total;
   KernelTimer kt_("prefill_kernel", stream);
-  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)total), dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream,
-                     p, nrb);
+  hipLaunchKernelGGL(prefill_kernel<D>, dim3(grid), dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream, p, nrb,
+                     persistent ? 1 : 0);
   return hipGetLastError();
 }
 
