@@ -215,54 +215,46 @@ struct WaveCtx {
 
 // Matrix phase: O^T += V^T P^T for the tile in slot SV (if PV), then
 // S^T = K Q^T for the tile in slot SK (if S).  S^T block kb holds keys
-// 32kb + 8(r/4) + 4half + r%4 of register r.  The 32 MFMAs run in chunks of
-// four, each chunk's LDS fragments read one chunk ahead (two chunks of
-// fragments live at a time, so the phase fits beside the wave's other
-// state); the S chunks alternate the two key blocks so that neighbouring
-// MFMAs are independent.
+// 32kb + 8(r/4) + 4half + r%4 of register r.  The LDS fragments stream
+// through a ring of eight registers: each MFMA's operand is read seven
+// MFMAs ahead of it (about 220 cycles of matrix work, more than an LDS read
+// takes while the other waves of its group read too).  The S MFMAs
+// alternate the two key blocks so that neighbouring MFMAs are independent.
 template <int D, int SK, int SV, bool PV, bool S>
 __device__ __forceinline__ void mfma_phase(WaveCtx<D>& w) {
   using T = Tile<D>;
   constexpr int KS = T::KS, DB = T::DB;
-  static_assert(DB <= 4, "one V^T fragment per d-block per chunk");
-  constexpr int NPV = PV ? 4 : 0;        // PV chunks: kk = 0..3, DB fragments each
-  constexpr int NS = S ? KS / 2 : 0;     // S chunks: k-steps 2c, 2c+1 of both key blocks
-  constexpr int N = NPV + NS;
+  constexpr int NPV = PV ? 4 * DB : 0;       // PV: kk-major, DB fragments per 16-key step
+  constexpr int N = NPV + (S ? 2 * KS : 0);  // S: per k-step, key blocks 0 and 1
+  constexpr int F = 8;                       // fragments in registers: F - 1 loads ahead
   if (S) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) w.s[kb][r] = 0.f;
   }
-  auto load = [&](int c, u32x4 (&f)[4]) {
-    if (c < NPV) {
-#pragma unroll
-      for (int q = 0; q < DB; ++q) f[q] = vt_frag<T::ROW_BYTES>(w.vp[q] + SV * T::MAT_BYTES + c * 16 * T::ROW_BYTES);
-    } else {
-      const int ks = 2 * (c - NPV);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        f[i] = *reinterpret_cast<const u32x4*>(w.kp[ks + (i >> 1)] + SK * T::MAT_BYTES + (i & 1) * 32 * T::ROW_BYTES);
-    }
+  auto load = [&](int i) -> u32x4 {
+    if (i < NPV) return vt_frag<T::ROW_BYTES>(w.vp[i % DB] + SV * T::MAT_BYTES + (i / DB) * 16 * T::ROW_BYTES);
+    const int j = i - NPV;
+    return *reinterpret_cast<const u32x4*>(w.kp[j >> 1] + SK * T::MAT_BYTES + (j & 1) * 32 * T::ROW_BYTES);
   };
-  auto mma = [&](int c, const u32x4 (&f)[4]) {
-    if (c < NPV) {
-#pragma unroll
-      for (int q = 0; q < DB; ++q) w.acc_o[q] = mfma(f[q], w.pf[c], w.acc_o[q]);
+  auto mma = [&](int i, u32x4 f) {
+    if (i < NPV) {
+      w.acc_o[i % DB] = mfma(f, w.pf[i / DB], w.acc_o[i % DB]);
     } else {
-      const int ks = 2 * (c - NPV);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w.s[i & 1] = mfma(f[i], w.qf[ks + (i >> 1)], w.s[i & 1]);
+      const int j = i - NPV;
+      w.s[j & 1] = mfma(f, w.qf[j >> 1], w.s[j & 1]);
     }
   };
   if (N == 0) return;
-  u32x4 f0[4], f1[4];
-  load(0, f0);
+  u32x4 f[F];
 #pragma unroll
-  for (int c = 0; c < N; ++c) {
-    if (c + 1 < N) load(c + 1, (c & 1) ? f0 : f1);
+  for (int i = 0; i < F - 1 && i < N; ++i) f[i] = load(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + F - 1 < N) f[(i + F - 1) % F] = load(i + F - 1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(c, (c & 1) ? f1 : f0);
+    mma(i, f[i % F]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
