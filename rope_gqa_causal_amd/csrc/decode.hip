@@ -411,19 +411,21 @@ __global__ void __launch_bounds__(64 * W) decode_loop_kernel(AttnParams p, int n
   }
 
   // Every load is unconditional: keys past the end re-read the last row and
-  // are masked in the scores.
+  // are masked in the scores.  Plain (temporal) loads: this kernel serves
+  // small batches, whose caches a generation reads again at every step and
+  // which the L2 and the MALL hold between steps.
   auto load = [&](u32x4 (&kf)[PASSES][4], u32x4 (&vf)[VLOADS], int kw) {
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int key = min(kw + ps * KPP + key_sub, L - 1);
       const bf16_t* kr = kbase + (int64_t)key * p.kv_ss;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kf[ps][i] = ld16_nt(kr + 8 * (part + LPK * i));
+      for (int i = 0; i < 4; ++i) kf[ps][i] = ld16(kr + 8 * (part + LPK * i));
     }
 #pragma unroll
     for (int t = 0; t < VLOADS; ++t) {
       const int key = min(kw + t * KPI + kq, L - 1);
-      vf[t] = ld16_nt(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
+      vf[t] = ld16(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
     }
   };
   // q (with ROPE: the lane's theta, the q and new-k pairs -- lanes past D/2
