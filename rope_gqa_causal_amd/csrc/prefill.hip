@@ -538,24 +538,44 @@ __device__ __forceinline__ void run_item(const AttnParams& p, char* lds, int gro
 
   // ---- epilogue: O = O^T / l, rounded to bf16 ----
   // acc_o[q] register r holds d = 32q + 8(r/4) + 4half + r%4 of column col.
+  // The rows go out through LDS: each wave writes its 32 rows into a block
+  // of its own (ring slots 3 and 4, which the next item's prologue copies do
+  // not touch; every wave has passed the final barriers, so no tile is read
+  // there any more), row-major with 16-byte chunks XOR-swizzled by the row,
+  // and reads them back as whole rows.  A store instruction then writes
+  // D/8 lanes' 16 bytes per row (a position's g heads are adjacent rows and
+  // adjacent in o) instead of 8 bytes of each of 32 rows.
   if (wt.last >= 0) {
+    constexpr int CH = T::CH;
     const float lsum = sum_halves(w.l_run);
-    if (col_ok) {
-      const float inv = 1.f / lsum;
-      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (tok0 + pos) * p.o_ss +
-                     (int64_t)h * p.o_sh;
+    const float inv = 1.f / lsum;
+    char* stage = lds + (wave < kWaves / 2 ? 0 : T::V_REGION) + 3 * T::MAT_BYTES + (wave & 3) * 32 * T::ROW_BYTES;
 #pragma unroll
-      for (int q = 0; q < DB; ++q)
+    for (int q = 0; q < DB; ++q)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = 32 * q + 8 * q4 + 4 * half;
-          u32x2 wv;
-          wv[0] = pack_bf16x2(w.acc_o[q][4 * q4] * inv, w.acc_o[q][4 * q4 + 1] * inv);
-          wv[1] = pack_bf16x2(w.acc_o[q][4 * q4 + 2] * inv, w.acc_o[q][4 * q4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d) = wv;
-        }
-      if (p.lse && half == 0) p.lse[lse_base + pos] = (w.m_run + log2f(lsum)) * kLn2;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = 4 * q + q4;  // 16-byte chunk of d = 32q + 8q4
+        u32x2 wv;
+        wv[0] = pack_bf16x2(w.acc_o[q][4 * q4] * inv, w.acc_o[q][4 * q4 + 1] * inv);
+        wv[1] = pack_bf16x2(w.acc_o[q][4 * q4 + 2] * inv, w.acc_o[q][4 * q4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(stage + col * T::ROW_BYTES + 16 * (c ^ (col % CH)) + 8 * half) = wv;
+      }
+    // A wave's LDS accesses complete in order, so its reads see its writes.
+    constexpr int RPI = 64 / CH;  // rows per read
+    const int c = lane % CH;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / CH;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * T::ROW_BYTES + 16 * (c ^ (r % CH)));
+      const int Rr = R0 + wave * 32 + r;
+      if (Rr < nrows) {
+        const int pr = Rr / group, hr = kvh * group + Rr % group;
+        bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (tok0 + pr) * p.o_ss +
+                       (int64_t)hr * p.o_sh;
+        *reinterpret_cast<u32x4*>(orow + 8 * c) = v;
+      }
     }
+    if (col_ok && p.lse && half == 0) p.lse[lse_base + pos] = (w.m_run + log2f(lsum)) * kLn2;
   }
 }
 
