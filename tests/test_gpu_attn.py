@@ -57,6 +57,37 @@ def test_prefill_bf16(case):
     assert (lse.cpu().double() - ref_lse).abs().max().item() < LSE_TOL_BF16
 
 
+# Grids with more row blocks than compute units run persistent workgroups
+# that walk several items each, prefetching the next item's Q and first
+# tiles; sequences start at different cache slots, so neighbouring items
+# differ in tile count.  Rows are checked by samples the oracle computes
+# one block at a time.
+PERSISTENT_CASES = [
+    # B, Sq, Hq, Hkv, D, q_start,                 S_max
+    (3, 1500, 24, 8, 128, [0, 300, 7], 1800),
+    (6, 1000, 12, 4, 64, [0, 5, 100, 0, 63, 1], 1100),
+    (8, 700, 16, 8, 32, [0, 1, 2, 3, 64, 65, 200, 0], 900),
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT_CASES, ids=lambda c: f"B{c[0]}Sq{c[1]}H{c[2]}/{c[3]}D{c[4]}")
+def test_prefill_persistent_grid_sampled_rows(case):
+    B, Sq, Hq, Hkv, D, q_start, S_max = case
+    q, kc, vc, qs = _prefill_case(B, Sq, Hq, Hkv, D, torch.bfloat16, q_start, S_max, Sq + D)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    o = rgc.gqa_attn_prefill(q.cuda(), kc.cuda(), vc.cuda(), qs.cuda(), lse=lse).cpu()
+    lse = lse.cpu().double()
+    sg = synth.generator(Sq)
+    for b in range(B):
+        s0 = int(torch.randint(0, Sq - 16, (1,), generator=sg))
+        for lo in (0, s0, Sq - 16):
+            rows = slice(lo, lo + 16)
+            ref, ref_lse = oracle.attn(q[b:b + 1, rows], kc[b:b + 1], vc[b:b + 1],
+                                       torch.tensor([q_start[b] + lo], dtype=torch.int32), want_lse=True)
+            assert_close(o[b:b + 1, rows], ref, torch.bfloat16, f"persistent prefill b={b} rows {lo}")
+            assert (lse[b:b + 1, :, rows] - ref_lse).abs().max().item() < LSE_TOL_BF16
+
+
 @pytest.mark.parametrize("case", [(1, 16, 4, 2, 32, [0], 24), (2, 70, 6, 3, 64, [0, 5], 80),
                                   (1, 40, 8, 2, 128, [3], 48)])
 def test_prefill_fp32(case):
