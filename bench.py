@@ -383,8 +383,9 @@ def decode_length_sweep(rgc, iters=20, cache_sets=3, lengths=(256, 512, 1024, 20
 
 def ceilings(iters=10):
     """What this GPU delivers to a hand-written kernel: a streaming read of
-    2 GiB with 16-byte loads, and back-to-back bf16 MFMA (32x32x16) on four
-    accumulators per wave (ceilings/ceilings.hip)."""
+    2 GiB with 16-byte loads, back-to-back bf16 MFMA (32x32x16) on four
+    accumulators per wave, and the same MFMA loop with every operand read
+    from LDS just before its use (ceilings/ceilings.hip)."""
     import ctypes
     path = os.path.join(ROOT, "ceilings", "libceil.so")
     if not os.path.exists(path):
@@ -393,6 +394,7 @@ def ceilings(iters=10):
     lib.ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_void_p]
     lib.ceil_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.ceil_lds_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     nbytes = 2 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
@@ -431,10 +433,35 @@ def ceilings(iters=10):
         tf = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
         mf_rows.append({"workgroups": wgs, "waves_per_simd": wgs * 4 // 1024, "TFLOP/s": round(tf, 1)})
         best_mf = max(best_mf, tf)
+    # LDS-fed matrix loop: 8 waves per workgroup (two per SIMD), each MFMA's
+    # B operand (16 bytes per lane, 1 KiB per wave) read from LDS; mode 0 is
+    # the same reads without the MFMAs (LDS read bandwidth).
+    lds_rows = {}
+    for mode in (0, 1):
+        wgs, loop = 512, 4096
+        out = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
+        if lib.ceil_lds_mfma(ctypes.c_void_p(out.data_ptr()), wgs, 64, mode, stream):
+            return {"error": "ceil_lds_mfma refused"}
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            lib.ceil_lds_mfma(ctypes.c_void_p(out.data_ptr()), wgs, loop, mode, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3
+        lds_bytes = float(wgs) * 8 * loop * 4 * 1024 * iters
+        if mode:
+            lds_rows["mfma_TFLOPs"] = round(float(wgs) * 8 * loop * 4 * 32768 * iters / sec / 1e12, 1)
+            lds_rows["lds_TBs_with_mfma"] = round(lds_bytes / sec / 1e12, 2)
+        else:
+            lds_rows["lds_TBs_reads_only"] = round(lds_bytes / sec / 1e12, 2)
     return {"hbm_read_GBs": round(best_read, 1), "hbm_read_frac_of_spec": round(best_read / HBM_PEAK_GBS, 4),
             "hbm_read_runs": read_rows,
             "mfma_bf16_TFLOPs": round(best_mf, 1), "mfma_bf16_frac_of_spec": round(best_mf / BF16_PEAK_TFLOPS, 4),
             "mfma_runs": mf_rows,
+            "lds_fed_mfma": dict(lds_rows, workgroups=512, waves_per_workgroup=8,
+                                 form="every MFMA's B operand read from LDS (16 B per lane) just before it"),
             "kernels": "ceilings/ceilings.hip: 16-byte reads of a 2 GiB buffer (8x the MALL) in several forms, "
                        "the best reported; v_mfma_f32_32x32x16_bf16 back to back on 4 accumulators per wave, no "
                        "memory traffic"}
