@@ -351,7 +351,7 @@ def decode_length_sweep(rgc, iters=20, cache_sets=3, lengths=(256, 512, 1024, 20
     for L in lengths:
         lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
         run = lambda i: rgc.gqa_attn_decode(q, sets[i % cache_sets][0], sets[i % cache_sets][1], lens, L, ws, out=o)
-        for i in range(3):
+        for i in range(10):
             run(i)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -487,7 +487,7 @@ class Diff:
         self.rgc.diff_attn_prefill(self.q1, self.q2, self.k1, self.k2, self.v, self.w.lam, out=self.o)
 
     def time(self, iters):
-        for _ in range(3):
+        for _ in range(10):
             self.run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -531,7 +531,7 @@ class DiffDecode:
     def time(self, iters):
         run = lambda i: self.rgc.diff_attn_decode(self.q1, self.q2, *self.sets[i % len(self.sets)], self.lens,
                                                   self.w.lam, self.S_max, self.ws, out=self.o)
-        for i in range(3):
+        for i in range(10):
             run(i)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -569,7 +569,7 @@ class Varlen:
 
     def time(self, iters):
         run = lambda: self.rgc.gqa_attn_prefill_varlen(self.q, self.k, self.v, self.cu, self.max_len, out=self.o)
-        for _ in range(3):
+        for _ in range(10):
             run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -703,7 +703,7 @@ def time_backward(rgc, synth, iters):
     ws = rgc.backward_workspace(w.B, w.S, w.Hq)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     run = lambda: rgc.gqa_attn_backward(q, k, v, o, d_o, lse, workspace=ws, dq=dq, dk=dk, dv=dv)
-    for _ in range(2):
+    for _ in range(5):
         run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -731,7 +731,7 @@ def time_prologues(pre, iters):
     for name, fn in (("rope_append", lambda: pre.rgc.rope_append(pre.q, pre.k, pre.v, pre.kc, pre.vc, pre.pos0)),
                      ("norm_rope_append", lambda: pre.rgc.norm_rope_append(pre.q, pre.k, pre.v, pre.kc, pre.vc,
                                                                           pre.pos0, eps=1e-6))):
-        for _ in range(3):
+        for _ in range(10):
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
