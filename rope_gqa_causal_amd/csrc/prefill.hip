@@ -27,14 +27,19 @@
 //    are in-lane except one v_permlane32_swap with the lane 32 away, and the
 //    probabilities are already in the B-operand layout of O^T = V^T P^T --
 //    P never leaves registers;
-//  * 64-key K and V tiles are staged HBM -> registers -> LDS through a
-//    4-slot ring: tile k + 3 is fetched during tile k's vector phase and
-//    stored during tile k + 1's, so its loads are in flight across a whole
-//    matrix phase; the barriers carry no wait for them.  Both tiles stay
-//    row-major in LDS with a per-row XOR swizzle of their 16-byte chunks: K
-//    fragments (A operand of S^T) are conflict-free 16-byte reads, and V^T
-//    fragments (A operand of O^T) come straight from the row-major V tile
-//    through ds_read_b64_tr_b16, the gfx950 transposing LDS read;
+//  * 64-key K and V tiles go HBM -> LDS by direct copies
+//    (global_load_lds_dwordx4, no registers) into a 5-slot ring, three tiles
+//    ahead of their first use; each wave waits only for its own copies of
+//    the tile the next phase needs, and the phase barrier publishes it.
+//    Both tiles stay row-major in LDS with a per-row XOR swizzle of their
+//    16-byte chunks: K fragments (A operand of S^T) are conflict-free
+//    16-byte reads, and V^T fragments (A operand of O^T) come straight from
+//    the row-major V tile through ds_read_b64_tr_b16, the gfx950 transposing
+//    LDS read;
+//  * the row sums add the bf16-rounded probabilities that meet V, read back
+//    out of the packed pairs with shifts and masks: the packed bf16 dot
+//    instruction would take one step instead of three, but it runs on the
+//    matrix pipeline and stalls the other wave's matrix instructions;
 //  * the running max is only raised (and O rescaled) when a tile's max
 //    exceeds it by more than 2^8, so the rescale is almost never taken; p is
 //    then at most 256, exact in fp32 and within bf16 range.  The tile max
@@ -42,8 +47,13 @@
 //    necessary condition for a p past 2^8): a wave's first tile and the
 //    rare raise -- the common tile does no max reduction at all;
 //  * the causal mask is applied on diagonal tiles only; tiles past a wave's
-//    last row are skipped (the wave still keeps the barriers); workgroups
-//    are issued heaviest row block first, XCD-aware.
+//    last row are skipped (the wave still keeps the barriers);
+//  * work order: (sequence, KV head) units stay on one XCD (shared L2),
+//    heaviest row blocks first; a grid with more row blocks than compute
+//    units runs one persistent workgroup per compute unit, each walking a
+//    list of row blocks dealt in snake order;
+//  * the output rows leave through LDS as whole rows (a store instruction
+//    covers D/8 lanes per row).
 #include <atomic>
 #include <type_traits>
 
