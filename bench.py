@@ -70,6 +70,12 @@ def parse():
     ap.add_argument("--summarize-counters", nargs="+", metavar="RUN_DIR",
                     help="turn rocprofv3 --pmc runs of `--phase prefill --with-ceilings` into "
                          "profiles/counters_prefill_mfma.json and exit")
+    ap.add_argument("--variants-only", action="store_true",
+                    help="time only the matrix-core variant lines (differential prefill and decode, "
+                         "packed-document prefill, backward) and exit: the counter runs of "
+                         "profiles/counters_variants.md")
+    ap.add_argument("--summarize-variant-counters", nargs="+", metavar="RUN_DIR",
+                    help="turn rocprofv3 --pmc runs of `--variants-only` into profiles/counters_variants.json")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE; both "
                          "with --copy-calibration) into profiles/counters_*.json and exit")
@@ -164,6 +170,63 @@ def summarize_pmc(fetch_dir, write_dir):
     record("decode_op", "decode.hip", ["decode_split_kernel", "decode_combine_kernel"],
            "the whole one-launch decode step (split + merge), average over the 32 decode calls of one bench step")
     record("prefill", "prefill.hip", ["prefill_kernel"], "one prefill launch of the bench step")
+
+
+VARIANT_KERNELS = ("diff_kernel", "diff_decode_kernel", "diff_combine_kernel", "prefill_kernel", "dq_kernel",
+                   "dkdv_kernel")
+
+
+def summarize_variant_counters(run_dirs):
+    """Per-dispatch averages of every counter found in the rocpd databases of
+    `--variants-only` runs, per kernel at its largest grid (the timed launch
+    shape), with the derived ratios of summarize_counters."""
+    import glob
+    import sqlite3
+    per = {}
+    for d in run_dirs:
+        for path in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+            rows = sqlite3.connect(path).execute(
+                "select dispatch_id, kernel_name, grid_size, counter_name, value from counters_collection").fetchall()
+            for did, kname, grid, cname, val in rows:
+                short = kname.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                short = short.split("<")[0].split("::")[-1]
+                if short not in VARIANT_KERNELS:
+                    continue
+                dd = per.setdefault((short, grid), {}).setdefault(cname, {})
+                key = (path, did)
+                if cname.startswith("GRBM_"):
+                    dd[key] = max(dd.get(key, 0.0), val)
+                else:
+                    dd[key] = dd.get(key, 0.0) + val
+    out = {}
+    for name in VARIANT_KERNELS:
+        grids = [g for (k, g) in per if k == name]
+        if not grids:
+            continue
+        cs = per[(name, max(grids))]
+        avg = {c: sum(v.values()) / len(v) for c, v in cs.items()}
+        mfma = avg.get("SQ_INSTS_MFMA", 0.0)
+        rec = {"grid_threads": max(grids), "counters_per_dispatch": {k: round(v, 1) for k, v in sorted(avg.items())}}
+        der = {}
+        if "MfmaUtil" in avg:
+            der["mfma_util"] = round(avg["MfmaUtil"] / 100.0, 4)
+        if "VALUBusy" in avg:
+            der["valu_busy"] = round(avg["VALUBusy"] / 100.0, 4)
+        if mfma and "SQ_INSTS_VALU" in avg:
+            der["other_valu_per_mfma"] = round((avg["SQ_INSTS_VALU"] - mfma) / mfma, 3)
+        if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+            der["valu_coexec_per_mfma_busy"] = round(avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+        if avg.get("SQ_LDS_IDX_ACTIVE"):
+            der["lds_conflict_per_active"] = round(avg.get("SQ_LDS_BANK_CONFLICT", 0.0) / avg["SQ_LDS_IDX_ACTIVE"], 4)
+        rec["derived"] = der
+        src = {"diff_kernel": "diff.hip", "diff_decode_kernel": "diff_decode.hip", "diff_combine_kernel": "diff_decode.hip",
+               "prefill_kernel": "prefill.hip", "dq_kernel": "backward_dq.hip", "dkdv_kernel": "backward.hip"}[name]
+        rec["kernel_sha"] = kernel_sha(src)
+        out[name] = rec
+    out["runs"] = list(run_dirs)
+    with open(os.path.join(PROFILES, "counters_variants.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def summarize_counters(run_dirs):
@@ -871,6 +934,9 @@ def main():
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
         return
+    if args.summarize_variant_counters:
+        summarize_variant_counters(args.summarize_variant_counters)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -881,6 +947,13 @@ def main():
     import rope_gqa_causal_amd as rgc
     from rope_gqa_causal_amd import synth
 
+    if args.variants_only:
+        res = {"diff_attn": Diff(rgc, synth).time(5),
+               "diff_attn_decode": DiffDecode(rgc, synth, args.cache_sets).time(10),
+               "varlen_prefill": Varlen(rgc, synth).time(5),
+               "backward": time_backward(rgc, synth, 3)}
+        print(json.dumps(res, ensure_ascii=False), flush=True)
+        return
     do_pre = args.phase in ("all", "prefill")
     do_dec = args.phase in ("all", "decode")
     print("[bench] setting up inputs", file=sys.stderr, flush=True)
