@@ -28,9 +28,10 @@
 //    probabilities are already in the B-operand layout of O^T = V^T P^T --
 //    P never leaves registers;
 //  * 64-key K and V tiles go HBM -> LDS by direct copies
-//    (global_load_lds_dwordx4, no registers) into a 5-slot ring, three tiles
-//    ahead of their first use; each wave waits only for its own copies of
-//    the tile the next phase needs, and the phase barrier publishes it.
+//    (global_load_lds_dwordx4, no registers) into a 5-slot ring, issued in
+//    the vector phase three tiles ahead of their first use; each wave waits
+//    only for its own copies of the tile the next phase needs, and the phase
+//    barrier publishes it.
 //    Both tiles stay row-major in LDS with a per-row XOR swizzle of their
 //    16-byte chunks: K fragments (A operand of S^T) are conflict-free
 //    16-byte reads, and V^T fragments (A operand of O^T) come straight from
@@ -323,12 +324,14 @@ struct WaveTiles {
 // SIMD runs a matrix phase while its B wave runs a vector phase, and the
 // other way round in the next interval.
 //
-// The ring: the matrix phase of tile t starts the wave's copy of tile t+3
+// The ring: the vector phase of tile t starts the wave's copy of tile t+3
 // into the slot tile t-2 used (its last readers, the matrix phases of tile
-// t-1 in both groups, are behind a barrier), and ends by waiting for its
-// copy of tile t+1 (started two matrix phases earlier); the barrier after
-// it publishes tile t+1, whose first reader is the matrix phase of tile
-// t+1 in group A, two barriers later.  A copy thus has five phases to land.
+// t-1 in both groups, are behind a barrier); the copies issue there, beside
+// the other group's matrix phase, because the matrix phase is the longer of
+// the two (its LDS fragment reads).  The matrix phase of tile t ends by
+// waiting for the wave's copy of tile t+1 (started two vector phases
+// earlier); the barrier after it publishes tile t+1, whose first reader is
+// the matrix phase of tile t+1 in group A, two barriers later.
 // SLOT = k % kSlots.
 template <int D, int SLOT>
 __device__ __forceinline__ void matrix_step(WaveCtx<D>& w, const Stager<D>& sg, uint32_t lds0, const char* kb,
@@ -336,7 +339,6 @@ __device__ __forceinline__ void matrix_step(WaveCtx<D>& w, const Stager<D>& sg, 
                                             const WaveTiles& wt, int wave, int lane) {
   using T = Tile<D>;
   constexpr int SPREV = (SLOT + kSlots - 1) % kSlots;
-  if (k + 3 < nkt) dma_tile<D, (SLOT + 3) % kSlots>(sg, lds0, kb, vb, kv_ss, (k + 3) * kKT, kmax, wave, lane);
   // k < nkt here.  A wave past its last tile still forms S (discarded: no
   // vector phase follows) in the step that adds its last PV, so the loop
   // carries one form of the phase.
@@ -345,15 +347,17 @@ __device__ __forceinline__ void matrix_step(WaveCtx<D>& w, const Stager<D>& sg, 
   } else if (k - 1 <= wt.last) {
     mfma_phase<D, SLOT, SPREV, true, true>(w);
   }
-  // tile k+1 landed: the copies of tiles k+2 and k+3 may still be in flight
-  if (k + 3 < nkt) tile_dma_wait<2 * T::LOADS>();
-  else if (k + 2 < nkt) tile_dma_wait<T::LOADS>();
+  // tile k+1 landed: the copy of tile k+2 may still be in flight
+  if (k + 2 < nkt) tile_dma_wait<T::LOADS>();
   else tile_dma_wait<0>();
   phase_barrier();
 }
 
-template <int D>
-__device__ __forceinline__ void vector_step(WaveCtx<D>& w, int t, const WaveTiles& wt) {
+template <int D, int SLOT>
+__device__ __forceinline__ void vector_step(WaveCtx<D>& w, const Stager<D>& sg, uint32_t lds0, const char* kb,
+                                            const char* vb, int64_t kv_ss, int t, int nkt, int kmax,
+                                            const WaveTiles& wt, int wave, int lane) {
+  if (t + 3 < nkt) dma_tile<D, (SLOT + 3) % kSlots>(sg, lds0, kb, vb, kv_ss, (t + 3) * kKT, kmax, wave, lane);
   if (t <= wt.last) softmax_phase<D>(w, t * kKT, t >= wt.diag_from);
   phase_barrier();
 }
@@ -363,7 +367,7 @@ __device__ __forceinline__ void tile_step(WaveCtx<D>& w, const Stager<D>& sg, ui
                                           const char* vb, int64_t kv_ss, int k, int nkt, int kmax,
                                           const WaveTiles& wt, int wave, int lane) {
   matrix_step<D, SLOT>(w, sg, lds0, kb, vb, kv_ss, k, nkt, kmax, wt, wave, lane);
-  vector_step<D>(w, k, wt);
+  vector_step<D, SLOT>(w, sg, lds0, kb, vb, kv_ss, k, nkt, kmax, wt, wave, lane);
 }
 
 // One work item: row block rb of unit (sequence b, KV head kvh).  Every
@@ -478,7 +482,7 @@ __device__ __forceinline__ void run_item(const AttnParams& p, char* lds, int gro
   if (group_b) phase_barrier();
   // tile 0: S only
   matrix_step<D, 0>(w, sg, lds0, kb, vb, p.kv_ss, 0, nkt, kmax, wt, wave, lane);
-  vector_step<D>(w, 0, wt);
+  vector_step<D, 0>(w, sg, lds0, kb, vb, p.kv_ss, 0, nkt, kmax, wt, wave, lane);
   for (int k = 1; k < nkt; k += kSlots) {
     tile_step<D, 1>(w, sg, lds0, kb, vb, p.kv_ss, k, nkt, kmax, wt, wave, lane);
     if (k + 1 >= nkt) break;
