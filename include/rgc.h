@@ -278,8 +278,9 @@ int rgc_gqa_attn_backward(void* dq, void* dk, void* dv, const void* q, const voi
  *   scale      applied to both maps' scores (1/sqrt(D) is the usual value).
  * bf16 only (RGC_ERR_DTYPE otherwise); D must be 64, the head dim of each
  * map in the differential workload (RGC_ERR_HEADDIM otherwise); kv_ss in
- * [0, 2^24) elements (RGC_ERR_LAYOUT otherwise).  Each map is normalised by the sum of the bf16-rounded
- * weights it multiplies V with; o is rounded once from fp32.  A row whose
+ * [0, 2^24) elements (RGC_ERR_LAYOUT otherwise).  Each map's weights are
+ * summed in fp32 and rounded to bf16 where they multiply V; o is rounded
+ * once from fp32.  A row whose
  * slots fall outside the cache gets NaN and raises *err_flag.
  */
 int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2,

@@ -37,10 +37,11 @@
 //    16-byte reads, and V^T fragments (A operand of O^T) come straight from
 //    the row-major V tile through ds_read_b64_tr_b16, the gfx950 transposing
 //    LDS read;
-//  * the row sums add the bf16-rounded probabilities that meet V, read back
-//    out of the packed pairs with shifts and masks: the packed bf16 dot
-//    instruction would take one step instead of three, but it runs on the
-//    matrix pipeline and stalls the other wave's matrix instructions;
+//  * the row sums add the probabilities in fp32 before they are rounded to
+//    bf16 for the PV product (each weight is then off by at most half a
+//    bf16 ulp, unbiased); no matrix-pipeline instruction (such as the packed
+//    bf16 dot) runs in the vector phase, where it would stall the other
+//    wave's matrix instructions;
 //  * the running max is only raised (and O rescaled) when a tile's max
 //    exceeds it by more than 2^8, so the rescale is almost never taken; p is
 //    then at most 256, exact in fp32 and within bf16 range.  The tile max
@@ -247,13 +248,8 @@ __device__ __forceinline__ void softmax_phase(WaveCtx<D>& w, int j0, bool mask) 
         w.s[kb][r] = fminf(w.s[kb][r], bound);
       }
   }
-  // p = 2^(s*c - m) with the running max m, rounded to bf16 for the PV
-  // product; the row sum adds the same rounded values, so the numerator and
-  // the denominator use identical weights.  The rounded values are read
-  // back out of the packed pair (a bf16 is the top half of a float) and
-  // added in fp32: the packed bf16 dot instruction would do the same in one
-  // step, but it runs on the matrix pipeline and stalls the other wave's
-  // matrix instructions, while shifts, masks and adds issue beside them.
+  // p = 2^(s*c - m) with the running max m; the row sum adds p in fp32 and
+  // the PV product takes p rounded to bf16.
   float ps;
   auto probs = [&]() {
     float ps0 = 0.f, ps1 = 0.f, ps2 = 0.f, ps3 = 0.f;
@@ -263,15 +259,13 @@ __device__ __forceinline__ void softmax_phase(WaveCtx<D>& w, int j0, bool mask) 
       for (int e = 0; e < 4; ++e) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(w.s[kk >> 1][8 * (kk & 1) + 2 * e], w.c, -w.m_run));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(w.s[kk >> 1][8 * (kk & 1) + 2 * e + 1], w.c, -w.m_run));
-        const uint32_t pk = pack_bf16x2(p0, p1);
-        w.pf[kk][e] = pk;
-        const float r0 = __builtin_bit_cast(float, pk << 16), r1 = __builtin_bit_cast(float, pk & 0xffff0000u);
+        w.pf[kk][e] = pack_bf16x2(p0, p1);
         if (e & 1) {
-          ps2 += r0;
-          ps3 += r1;
+          ps2 += p0;
+          ps3 += p1;
         } else {
-          ps0 += r0;
-          ps1 += r1;
+          ps0 += p0;
+          ps1 += p1;
         }
       }
     }
