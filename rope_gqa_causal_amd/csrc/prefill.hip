@@ -230,7 +230,7 @@ __device__ __forceinline__ void mfma_phase(WaveCtx<D>& w) {
 
 // Vector phase of the tile starting at key j0: mask (diagonal tiles),
 // online softmax (log2 domain), P^T rounded to bf16 into w.pf.
-template <int D>
+template <int D, bool FIRST>
 __device__ __forceinline__ void softmax_phase(WaveCtx<D>& w, int j0, bool mask) {
   constexpr int DB = Tile<D>::DB;
   if (mask) {  // wave-uniform: diagonal tiles only
@@ -271,14 +271,7 @@ __device__ __forceinline__ void softmax_phase(WaveCtx<D>& w, int j0, bool mask) 
     }
     ps = (ps0 + ps1) + (ps2 + ps3);
   };
-  probs();
-  // The running max is raised (and O rescaled) only when the tile's max
-  // exceeds it by more than the threshold, i.e. only if some p > 2^8 -- and
-  // then the lane's sum of p exceeds 2^8 as well.  So the tile max is taken
-  // only on tiles where some lane's sum does (a wave's first tile, where
-  // m = -inf gives p = inf; a new max past the threshold; overflow): a rare,
-  // wave-uniform branch that raises m, rescales and recomputes p.
-  if (__builtin_amdgcn_ballot_w64(!(ps <= kSumTrigger))) {
+  auto tile_max = [&]() {
     float m0 = fmaxf(fmaxf(w.s[0][0], w.s[0][1]), w.s[0][2]);
     float m1 = fmaxf(fmaxf(w.s[1][0], w.s[1][1]), w.s[1][2]);
 #pragma unroll
@@ -288,7 +281,26 @@ __device__ __forceinline__ void softmax_phase(WaveCtx<D>& w, int j0, bool mask) 
     }
     m0 = fmaxf(fmaxf(m0, w.s[0][15]), m1);
     m0 = fmaxf(m0, w.s[1][15]);
-    const float tmax = max_halves(m0) * w.c;
+    return max_halves(m0) * w.c;
+  };
+  if constexpr (FIRST) {
+    // A wave's first tile (m = -inf, O = 0, l = 0): the tile max becomes the
+    // running max, then the probabilities are formed once.  Key 0 is kept in
+    // every column, so the max is finite.
+    w.m_run = tile_max();
+    probs();
+    w.l_run = ps;
+    return;
+  }
+  probs();
+  // The running max is raised (and O rescaled) only when the tile's max
+  // exceeds it by more than the threshold, i.e. only if some p > 2^8 -- and
+  // then the lane's sum of p exceeds 2^8 as well.  So the tile max is taken
+  // only on tiles where some lane's sum does (a wave's first tile, where
+  // m = -inf gives p = inf; a new max past the threshold; overflow): a rare,
+  // wave-uniform branch that raises m, rescales and recomputes p.
+  if (__builtin_amdgcn_ballot_w64(!(ps <= kSumTrigger))) {
+    const float tmax = tile_max();
     const float m_new = tmax > w.m_run + kRescaleThreshold ? tmax : w.m_run;
     float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);  // 0 on the first tile
     // alpha passes through an empty asm, so the multiplications below
@@ -347,12 +359,12 @@ __device__ __forceinline__ void matrix_step(WaveCtx<D>& w, const Stager<D>& sg, 
   phase_barrier();
 }
 
-template <int D, int SLOT>
+template <int D, int SLOT, bool FIRST = false>
 __device__ __forceinline__ void vector_step(WaveCtx<D>& w, const Stager<D>& sg, uint32_t lds0, const char* kb,
                                             const char* vb, int64_t kv_ss, int t, int nkt, int kmax,
                                             const WaveTiles& wt, int wave, int lane) {
   if (t + 3 < nkt) dma_tile<D, (SLOT + 3) % kSlots>(sg, lds0, kb, vb, kv_ss, (t + 3) * kKT, kmax, wave, lane);
-  if (t <= wt.last) softmax_phase<D>(w, t * kKT, t >= wt.diag_from);
+  if (t <= wt.last) softmax_phase<D, FIRST>(w, t * kKT, t >= wt.diag_from);
   phase_barrier();
 }
 
@@ -476,7 +488,7 @@ __device__ __forceinline__ void run_item(const AttnParams& p, char* lds, int gro
   if (group_b) phase_barrier();
   // tile 0: S only
   matrix_step<D, 0>(w, sg, lds0, kb, vb, p.kv_ss, 0, nkt, kmax, wt, wave, lane);
-  vector_step<D, 0>(w, sg, lds0, kb, vb, p.kv_ss, 0, nkt, kmax, wt, wave, lane);
+  vector_step<D, 0, true>(w, sg, lds0, kb, vb, p.kv_ss, 0, nkt, kmax, wt, wave, lane);
   for (int k = 1; k < nkt; k += kSlots) {
     tile_step<D, 1>(w, sg, lds0, kb, vb, p.kv_ss, k, nkt, kmax, wt, wave, lane);
     if (k + 1 >= nkt) break;
