@@ -213,7 +213,7 @@ __device__ __forceinline__ void mfma_phase(DiffWave<D>& w) {
 
 // Vector phase of map MAP for the tile starting at key j0: mask (diagonal
 // tiles), online softmax (log2 domain), P^T rounded to bf16 into w.pf[MAP].
-template <int D, int MAP>
+template <int D, int MAP, bool FIRST>
 __device__ __forceinline__ void softmax_map(DiffWave<D>& w, int j0, bool mask) {
   constexpr int DB = DTile<D>::DB;
   f32x16& s = w.s[MAP];
@@ -251,13 +251,7 @@ __device__ __forceinline__ void softmax_map(DiffWave<D>& w, int j0, bool mask) {
     }
     ps = (ps0 + ps1) + (ps2 + ps3);
   };
-  probs();
-  // A tile max past the running max by more than the threshold makes some
-  // p > 2^8 and the lane's sum > 2^8 too; so the max is only taken when some
-  // lane's sum passes 2^8 (a wave's first keys, against kNoMax, make it
-  // infinite): a rare, wave-uniform branch that raises m, rescales O and l
-  // and recomputes p.  Masked scores are -inf and give p = 0 throughout.
-  if (__builtin_amdgcn_ballot_w64(!(ps <= kSumTrigger))) {
+  auto tile_max = [&]() {
     float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]);
     float m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
 #pragma unroll
@@ -265,7 +259,25 @@ __device__ __forceinline__ void softmax_map(DiffWave<D>& w, int j0, bool mask) {
       m0 = fmaxf(m0, s[r]);
       m1 = fmaxf(m1, s[r + 1]);
     }
-    const float tmax = max_halves(fmaxf(m0, m1)) * w.c;
+    return max_halves(fmaxf(m0, m1)) * w.c;
+  };
+  if constexpr (FIRST) {
+    // The wave's first tile (m = kNoMax, O = 0, l = 0): the tile max becomes
+    // the running max, then the probabilities are formed once.  A column with
+    // no key in this wave's half of the tile keeps kNoMax (its p are 0).
+    w.m_run[MAP] = fmaxf(tile_max(), kNoMax);
+    probs();
+    w.l_run[MAP] = ps;
+    return;
+  }
+  probs();
+  // A tile max past the running max by more than the threshold makes some
+  // p > 2^8 and the lane's sum > 2^8 too; so the max is only taken when some
+  // lane's sum passes 2^8 (a wave's first keys, against kNoMax, make it
+  // infinite): a rare, wave-uniform branch that raises m, rescales O and l
+  // and recomputes p.  Masked scores are -inf and give p = 0 throughout.
+  if (__builtin_amdgcn_ballot_w64(!(ps <= kSumTrigger))) {
+    const float tmax = tile_max();
     const float m_new = tmax > w.m_run[MAP] + kRescaleThreshold ? tmax : w.m_run[MAP];
     float alpha = __builtin_amdgcn_exp2f(w.m_run[MAP] - m_new);  // 0 when m_run was kNoMax
     // alpha passes through an empty asm, so the multiplications below stay
@@ -322,12 +334,12 @@ __device__ __forceinline__ void matrix_step(DiffWave<D>& w, const DStager<D>& sg
   phase_barrier();
 }
 
-template <int D>
+template <int D, bool FIRST = false>
 __device__ __forceinline__ void vector_step(DiffWave<D>& w, int t, const WaveTiles& wt) {
   if (t <= wt.last) {
     const bool mask = t >= wt.diag_from;
-    softmax_map<D, 0>(w, t * kKT, mask);
-    softmax_map<D, 1>(w, t * kKT, mask);
+    softmax_map<D, 0, FIRST>(w, t * kKT, mask);
+    softmax_map<D, 1, FIRST>(w, t * kKT, mask);
   }
   phase_barrier();
 }
@@ -452,7 +464,7 @@ __global__ void __launch_bounds__(kThreads, 1) diff_kernel(DiffParams dp, int nq
   if (kh) phase_barrier();
   // tile 0: S only
   matrix_step<D, 0>(w, sg, lds0, p.kv_ss, 0, nkt, kmax, wt, wave, lane);
-  vector_step<D>(w, 0, wt);
+  vector_step<D, true>(w, 0, wt);
   for (int k = 1; k < nkt; k += kSlots) {
     tile_step<D, 1>(w, sg, lds0, p.kv_ss, k, nkt, kmax, wt, wave, lane);
     if (k + 1 >= nkt) break;
