@@ -530,6 +530,24 @@ def ceilings(iters=10):
                        "memory traffic"}
 
 
+def warm_up(run, min_ms=25.0, min_calls=10):
+    """Untimed calls before a variant line's timed ones: at least min_calls
+    and at least min_ms of GPU work, about what the step's own ten warm-up
+    steps give (the shader clock rises over the first tens of milliseconds
+    of load, so a line timed after a few calls of a short kernel reads its
+    ramp rather than its settled rate).  run(i) takes the call index."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while i < min_calls or (time.perf_counter() - t0) * 1e3 < min_ms:
+        run(i)
+        i += 1
+        if i % 5 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
 class Diff:
     """Differential attention on its own workload (B 4 x 1024 tokens, 16 q /
     8 KV heads, two maps of head dim 64, lambda 0.8); timed apart from the
@@ -550,9 +568,7 @@ class Diff:
         self.rgc.diff_attn_prefill(self.q1, self.q2, self.k1, self.k2, self.v, self.w.lam, out=self.o)
 
     def time(self, iters):
-        for _ in range(10):
-            self.run()
-        torch.cuda.synchronize()
+        warm_up(lambda i: self.run())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(iters):
@@ -594,9 +610,7 @@ class DiffDecode:
     def time(self, iters):
         run = lambda i: self.rgc.diff_attn_decode(self.q1, self.q2, *self.sets[i % len(self.sets)], self.lens,
                                                   self.w.lam, self.S_max, self.ws, out=self.o)
-        for i in range(10):
-            run(i)
-        torch.cuda.synchronize()
+        warm_up(run)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(iters):
@@ -632,9 +646,7 @@ class Varlen:
 
     def time(self, iters):
         run = lambda: self.rgc.gqa_attn_prefill_varlen(self.q, self.k, self.v, self.cu, self.max_len, out=self.o)
-        for _ in range(10):
-            run()
-        torch.cuda.synchronize()
+        warm_up(lambda i: run())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(iters):
@@ -766,9 +778,7 @@ def time_backward(rgc, synth, iters):
     ws = rgc.backward_workspace(w.B, w.S, w.Hq)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     run = lambda: rgc.gqa_attn_backward(q, k, v, o, d_o, lse, workspace=ws, dq=dq, dk=dk, dv=dv)
-    for _ in range(5):
-        run()
-    torch.cuda.synchronize()
+    warm_up(lambda i: run(), min_calls=5)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
@@ -794,9 +804,7 @@ def time_prologues(pre, iters):
     for name, fn in (("rope_append", lambda: pre.rgc.rope_append(pre.q, pre.k, pre.v, pre.kc, pre.vc, pre.pos0)),
                      ("norm_rope_append", lambda: pre.rgc.norm_rope_append(pre.q, pre.k, pre.v, pre.kc, pre.vc,
                                                                           pre.pos0, eps=1e-6))):
-        for _ in range(10):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(lambda i: fn())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(iters):
