@@ -494,7 +494,8 @@ __global__ void __launch_bounds__(kThreads, 1) diff_kernel(DiffParams dp, int nq
   // waves 4-7 leave their partial results (O^T, m, l of both maps) in the
   // K1/K2 regions, laid out [value][lane] in 16-byte units so that a wave's
   // stores and its partner's loads are whole-row accesses; waves 0-3 stage
-  // the output rows in the V region.
+  // the output rows in the V region and store them with the nontemporal
+  // hint (o is not read again here).
   constexpr int kPartUnits = 2 * DB * 4 + 1;  // 16-byte units per lane: O^T of both maps, then m, l
   static_assert(kWaves / 2 * kPartUnits * 64 * 16 <= 2 * T::REGION, "partials fit the K1 and K2 regions");
   char* part = lds + (wave & 3) * kPartUnits * 64 * 16 + 16 * lane;
@@ -561,7 +562,7 @@ __global__ void __launch_bounds__(kThreads, 1) diff_kernel(DiffParams dp, int nq
       if (s < p.Sq) {
         bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (int64_t)s * p.o_ss +
                        (int64_t)h * p.o_sh;
-        *reinterpret_cast<u32x4*>(orow + 8 * c) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(orow + 8 * c));
       }
     }
   }

@@ -521,7 +521,10 @@ __device__ __forceinline__ void run_item(const AttnParams& p, char* lds, int gro
   // there any more), row-major with 16-byte chunks XOR-swizzled by the row,
   // and reads them back as whole rows.  A store instruction then writes
   // D/8 lanes' 16 bytes per row (a position's g heads are adjacent rows and
-  // adjacent in o) instead of 8 bytes of each of 32 rows.
+  // adjacent in o) instead of 8 bytes of each of 32 rows.  The rows are
+  // stored with the nontemporal hint: o is not read again here, and the L2
+  // keeps the K/V tiles that later row blocks of the unit read (the q loads
+  // keep the default: each q line serves four of a wave's loads).
   if (wt.last >= 0) {
     constexpr int CH = T::CH;
     const float lsum = sum_halves(w.l_run);
@@ -549,7 +552,7 @@ __device__ __forceinline__ void run_item(const AttnParams& p, char* lds, int gro
         const int pr = Rr / group, hr = kvh * group + Rr % group;
         bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (tok0 + pr) * p.o_ss +
                        (int64_t)hr * p.o_sh;
-        *reinterpret_cast<u32x4*>(orow + 8 * c) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(orow + 8 * c));
       }
     }
     if (col_ok && p.lse && half == 0) p.lse[lse_base + pos] = (w.m_run + log2f(lsum)) * kLn2;
