@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
                     help="target wall time of each CPU-oracle sample (decode, prefill)")
     ap.add_argument("--cache-sets", type=int, default=3,
                     help="independent decode cache sets rotated call by call (1 = no rotation)")
@@ -964,6 +964,7 @@ def main():
         return
     do_pre = args.phase in ("all", "prefill")
     do_dec = args.phase in ("all", "decode")
+    t_run = time.perf_counter()
     print("[bench] setting up inputs", file=sys.stderr, flush=True)
     pre = Prefill(rgc, synth) if do_pre else None
     dec = Decode(rgc, synth, args.cache_sets) if do_dec else None
@@ -980,7 +981,7 @@ def main():
         if do_dec:
             dec.run()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] warmup done ({args.warmup} steps) ({time.perf_counter() - t_run:.1f} s)", file=sys.stderr, flush=True)
 
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -1004,7 +1005,7 @@ def main():
         phase.append((a, m, z))
     t_end.record()
     torch.cuda.synchronize()
-    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] timed {args.steps} steps ({time.perf_counter() - t_run:.1f} s)", file=sys.stderr, flush=True)
 
     total_ms = t_start.elapsed_time(t_end)
     result = {
@@ -1114,16 +1115,17 @@ def main():
         result["varlen_prefill"] = Varlen(rgc, synth).time(max(args.steps, 5))
         result["backward"] = time_backward(rgc, synth, max(args.steps, 3))
         result["generation_125m"] = Generation(rgc, synth).time()
-        print("[bench] timed the variant lines", file=sys.stderr, flush=True)
+        print(f"[bench] timed the variant lines ({time.perf_counter() - t_run:.1f} s)", file=sys.stderr, flush=True)
         result["decode_length_sweep"] = decode_length_sweep(rgc, cache_sets=max(args.cache_sets, 1))
         result["ceilings"] = ceilings()
-        print("[bench] timed the length sweep and the ceilings", file=sys.stderr, flush=True)
+        print(f"[bench] timed the length sweep and the ceilings ({time.perf_counter() - t_run:.1f} s)", file=sys.stderr, flush=True)
     elif args.with_ceilings:
         result["ceilings"] = ceilings(iters=2)
     result["pages_context"] = PAGES_CONTEXT
     if not args.no_cpu_baseline and args.phase == "all":
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        print(f"[bench] timing the CPU oracle ({time.perf_counter() - t_run:.1f} s)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pre, dec, args.cpu_seconds)
+    print(f"[bench] done ({time.perf_counter() - t_run:.1f} s)", file=sys.stderr, flush=True)
     print(json.dumps(result, ensure_ascii=False), flush=True)
 
 
