@@ -30,10 +30,11 @@
 //    phase (both maps' mask, online softmax and bf16 probabilities); waves
 //    0-3 and 4-7 run them one barrier apart, so one wave's softmax issues
 //    beside the other wave's matrix instructions;
-//  * each map's running max is raised lazily (only when a tile's max passes
-//    it by 2^8; the tile max is only taken when a lane's sum of
-//    probabilities passes 2^8); the row sums add the probabilities in fp32
-//    before they are rounded to bf16 for the PV product;
+//  * each map's running max is set by a wave's first tile and then raised
+//    lazily (only when a tile's max passes it by 2^8; the tile max is only
+//    taken when a lane's sum of probabilities passes 2^8); the row sums add
+//    the probabilities in fp32 before they are rounded to bf16 for the PV
+//    product;
 //  * the epilogue forms o1 / l1 - lambda * o2 / l2, rounds once to bf16 and
 //    writes whole rows through LDS.
 #include "common.h"

@@ -45,9 +45,9 @@
 //  * the running max is only raised (and O rescaled) when a tile's max
 //    exceeds it by more than 2^8, so the rescale is almost never taken; p is
 //    then at most 256, exact in fp32 and within bf16 range.  The tile max
-//    itself is only computed when some lane's tile sum of p passes 2^8 (a
-//    necessary condition for a p past 2^8): a wave's first tile and the
-//    rare raise -- the common tile does no max reduction at all;
+//    itself is only computed on a wave's first tile (where it becomes the
+//    running max) and when some lane's tile sum of p passes 2^8 (a necessary
+//    condition for a p past 2^8) -- the common tile does no max reduction;
 //  * the causal mask is applied on diagonal tiles only; tiles past a wave's
 //    last row are skipped (the wave still keeps the barriers);
 //  * work order: (sequence, KV head) units stay on one XCD (shared L2),
