@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -82,9 +83,30 @@ def parse():
     return ap.parse_args()
 
 
+def _code_text(name, seen):
+    """The code of csrc/<name> and of the local headers it includes, with
+    comments and whitespace removed (so that a comment edit keeps the stored
+    counters, and a change to a header the kernel includes does not)."""
+    if name in seen:
+        return ""
+    seen.add(name)
+    path = os.path.join(ROOT, "rope_gqa_causal_amd", "csrc", name)
+    if not os.path.exists(path):
+        return ""
+    with open(path) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    parts = [re.sub(r"\s+", " ", src).strip()]
+    for inc in re.findall(r'#include\s+"([^"]+)"', src):
+        parts.append(_code_text(inc, seen))
+    return "\n".join(parts)
+
+
 def kernel_sha(name):
-    with open(os.path.join(ROOT, "rope_gqa_causal_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code (see _code_text), recorded with the
+    counters taken on it."""
+    return hashlib.sha256(_code_text(name, set()).encode()).hexdigest()[:16]
 
 
 def stored_traffic(kind, src, launches_bytes):
