@@ -14,10 +14,10 @@
 //    waves 4-7 its keys 32-63.  The two waves of a SIMD thus always hold
 //    equal work, and each keeps its own running max, sum and O^T per map,
 //    merged through LDS at the end (the usual combination of two partial
-//    softmaxes over disjoint keys).  Workgroups are launched heaviest query
-//    tile first over all heads, so a compute unit that finishes a light
-//    tile takes the next heaviest: the causal work evens out without a
-//    split of any row's keys across workgroups;
+//    softmaxes over disjoint keys).  Each workgroup runs two such items in
+//    turn, a head's heavier and lighter query tile (see diff_kernel), so
+//    the causal work evens out over the workgroups without a split of any
+//    row's keys, and the second item needs no workgroup launch;
 //  * scores are computed transposed (S^T = K Q^T, keys in the MFMA M
 //    dimension): a lane holds one query's column, each map's softmax is
 //    in-lane plus one v_permlane32_swap, and the bf16 probabilities are
@@ -353,22 +353,12 @@ __device__ __forceinline__ void tile_step(DiffWave<D>& w, const DStager<D>& sg, 
   vector_step<D>(w, k, wt);
 }
 
-// Work order: workgroup i = rank * (B * Hq) + head takes query tile
-// nqt-1-rank of that head, so the grid starts with every head's heaviest
-// tile and each later workgroup is no heavier than those before it: a
-// compute unit that frees up takes the heaviest tile left.  Workgroup i runs
-// on XCD i % 8, so a head stays on one XCD (its K1, K2 and V in one L2).
+// One item: query tile qt (128 positions) of one head, both maps.
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) diff_kernel(DiffParams dp, int nqt) {
+__device__ __forceinline__ void diff_item(const DiffParams& dp, char* lds, int qt, int head) {
   using T = DTile<D>;
   constexpr int KS = T::KS, DB = T::DB;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
   const AttnParams& p = dp.a;
-
-  const int heads = p.B * p.Hq;
-  const int rank = (int)blockIdx.x / heads, head = (int)blockIdx.x % heads;
-  if (rank >= nqt) return;
-  const int qt = nqt - 1 - rank;
   const int b = head / p.Hq, h = head % p.Hq;
   const int kvh = h / (p.Hq / p.Hkv);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -569,11 +559,32 @@ __global__ void __launch_bounds__(kThreads, 1) diff_kernel(DiffParams dp, int nq
   }
 }
 
+// Work order: workgroup g takes head g % (B * Hq) and, for pair index
+// pr = g / (B * Hq), that head's query tiles nqt-1-pr (the heavier) and pr
+// (the lighter), one after the other: every workgroup carries the same
+// number of key tiles (at nqt = 8, sixteen and two, fourteen and four, ...),
+// the heavy pairs start first, and the second item needs no workgroup
+// launch.  Workgroup g runs on XCD g % 8, so (with B * Hq a multiple of 8)
+// both items of a head stay on one XCD: the lighter item's K1, K2 and V are
+// a prefix of what the heavier one read into that L2.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) diff_kernel(DiffParams dp, int nqt) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int heads = dp.a.B * dp.a.Hq;
+  const int head = (int)blockIdx.x % heads, pr = (int)blockIdx.x / heads;
+  const int items = pr < nqt - 1 - pr ? 2 : 1;
+#pragma clang loop unroll(disable)
+  for (int it = 0; it < items; ++it) {
+    if (it) phase_barrier();  // every wave is done with the ring, partials and staging
+    diff_item<D>(dp, lds, it ? pr : nqt - 1 - pr, head);
+  }
+}
+
 template <int D>
 hipError_t launch_d(const DiffParams& dp, hipStream_t stream) {
   const AttnParams& p = dp.a;
   const int nqt = (p.Sq + kQT - 1) / kQT;
-  const int64_t total = (int64_t)p.B * p.Hq * nqt;
+  const int64_t total = (int64_t)p.B * p.Hq * ((nqt + 1) / 2);
   KernelTimer kt_("diff_kernel", stream);
   hipLaunchKernelGGL(diff_kernel<D>, dim3((unsigned)total), dim3(kThreads), (size_t)DTile<D>::LDS_BYTES, stream,
                      dp, nqt);
