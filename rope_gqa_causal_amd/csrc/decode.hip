@@ -15,11 +15,15 @@
 //  * every K and V byte of the chunk is read exactly once, with 16-byte
 //    loads, and serves all the query heads of the group (up to 4 per
 //    workgroup);
-//  * every load of a wave is unconditional and issued before any
-//    arithmetic: keys past the end re-read the last row and are masked in
-//    the scores.  (A guarded load per key makes the compiler wait for all
-//    earlier loads at each guard, which serialises the wave's memory
-//    traffic.)
+//  * every load of a wave is unconditional: keys past the end re-read the
+//    last row and are masked in the scores.  (A guarded load per key makes
+//    the compiler wait for all earlier loads at each guard, which
+//    serialises the wave's memory traffic.)  The K rows of all the wave's
+//    keys go out before any arithmetic; the V rows of a q.k pass's keys go
+//    out right after that pass's scores, into the registers its K rows
+//    leave free, so K and V never hold separate register sets and three
+//    workgroups fit a compute unit (two when all loads went out first:
+//    6 % slower per call on the ragged batch);
 //  * q.k uses packed bf16 dot products (v_dot2_f32_bf16) over a 4-lane key
 //    layout that needs only two quad swizzles per key; the probabilities go
 //    through LDS to a second layout in which each lane accumulates 8 output
@@ -182,12 +186,7 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
 #pragma unroll
       for (int i = 0; i < 4; ++i) kf[ps][i] = ld16_nt(kr + 8 * (part + LPK * i));
     }
-#pragma unroll
-    for (int t = 0; t < VLOADS; ++t) {
-      const int key = min(kw + t * KPI + kq, L - 1);
-      vf[t] = ld16_nt(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
+    __builtin_amdgcn_sched_barrier(0);  // keep the K loads ahead of the arithmetic
 
     if constexpr (ROPE) {
       // Pair m = lane turns by (L - 1) theta_m (same angle, rotation and
@@ -220,9 +219,6 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
           if (min(kw + ps * KPP + key_sub, L - 1) == L - 1)
 #pragma unroll
             for (int i = 0; i < 4; ++i) kf[ps][i] = kn[i];
-#pragma unroll
-        for (int t = 0; t < VLOADS; ++t)
-          if (min(kw + t * KPI + kq, L - 1) == L - 1) vf[t] = vn;
         if (hs == 0) {
           bf16_t* kc = reinterpret_cast<bf16_t*>(r.k_cache) + (int64_t)b * p.kv_sb + (int64_t)kvh * p.kv_sh +
                        (int64_t)(L - 1) * p.kv_ss;
@@ -255,6 +251,16 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
         d = sum_within<LPK>(d);
         z[g][ps] = valid ? d * c : -INFINITY;
       }
+      // This pass's keys' V rows, into the registers its K rows leave free
+      // (so K and V never hold separate register sets: three workgroups
+      // fit a compute unit).
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = ps * (VLOADS / PASSES); t < (ps + 1) * (VLOADS / PASSES); ++t) {
+        const int key = min(kw + t * KPI + kq, L - 1);
+        vf[t] = ld16_nt(vbase + (int64_t)key * p.kv_ss + 8 * dgrp);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // ---- softmax over the wave's keys (replicated across a key's lanes) ----
 #pragma unroll
@@ -293,10 +299,17 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(AttnParams p,
       uint32_t pp[GS];
 #pragma unroll
       for (int g = 0; g < GS; ++g) pp[g] = pack_bf16x2(pa[g], pb[g]);
+      u32x4 va = vf[t], vb = vf[t + 1];
+      if constexpr (ROPE) {
+        if (last) {  // the new token's v for slot L - 1 (the cache slot is not written yet)
+          if (min(kw + t * KPI + kq, L - 1) == L - 1) va = vn;
+          if (min(kw + (t + 1) * KPI + kq, L - 1) == L - 1) vb = vn;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = __builtin_amdgcn_perm(vf[t + 1][e], vf[t][e], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(vf[t + 1][e], vf[t][e], 0x07060302u);
+        const uint32_t lo = __builtin_amdgcn_perm(vb[e], va[e], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(vb[e], va[e], 0x07060302u);
 #pragma unroll
         for (int g = 0; g < GS; ++g) {
           acc[g][2 * e] = dot2(pp[g], lo, acc[g][2 * e]);
