@@ -77,6 +77,8 @@ def parse():
                          "profiles/counters_variants.md")
     ap.add_argument("--summarize-variant-counters", nargs="+", metavar="RUN_DIR",
                     help="turn rocprofv3 --pmc runs of `--variants-only` into profiles/counters_variants.json")
+    ap.add_argument("--summarize-trace", metavar="RUN_DIR",
+                    help="print the per-kernel table of a rocprofv3 --kernel-trace run and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE; both "
                          "with --copy-calibration) into profiles/counters_*.json and exit")
@@ -192,6 +194,29 @@ def summarize_pmc(fetch_dir, write_dir):
     record("decode_op", "decode.hip", ["decode_split_kernel", "decode_combine_kernel"],
            "the whole one-launch decode step (split + merge), average over the 32 decode calls of one bench step")
     record("prefill", "prefill.hip", ["prefill_kernel"], "one prefill launch of the bench step")
+
+
+def summarize_trace(run_dir, top=40):
+    """Per kernel and launch shape (workgroups x threads, LDS bytes, VGPRs):
+    calls and average / min / max duration in us, from the database of a
+    rocprofv3 --kernel-trace run, as a markdown table ordered by total time."""
+    import glob
+    import sqlite3
+    groups = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*.db"), recursive=True):
+        rows = sqlite3.connect(path).execute(
+            "select name, grid_x, grid_y, grid_z, workgroup_x, workgroup_y, workgroup_z, lds_size, vgpr_count, "
+            "duration from kernels").fetchall()
+        for name, gx, gy, gz, wx, wy, wz, lds, vgpr, dur in rows:
+            short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            short = short.split("<")[0].split("::")[-1]
+            wgs = (gx // max(wx, 1)) * (gy // max(wy, 1)) * (gz // max(wz, 1))
+            key = (short, wgs, wx * wy * wz, lds, vgpr)
+            groups.setdefault(key, []).append(dur / 1e3)
+    print("| kernel | workgroups x threads | LDS bytes | VGPRs (trace field) | calls | avg us | min us | max us |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (k, wg, wx, lds, vgpr), d in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]:
+        print(f"| {k} | {wg} x {wx} | {lds} | {vgpr} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
 
 
 VARIANT_KERNELS = ("diff_kernel", "diff_decode_kernel", "diff_combine_kernel", "prefill_kernel", "dq_kernel",
@@ -958,6 +983,9 @@ PAGES_CONTEXT = {
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
