@@ -276,12 +276,17 @@ int rgc_gqa_attn_backward(void* dq, void* dk, void* dv, const void* q, const voi
  *   q_start    [B] int32 or NULL, as in rgc_gqa_attn_prefill.
  *   lambda     the constant weight of the second map (no re-normalisation).
  *   scale      applied to both maps' scores (1/sqrt(D) is the usual value).
- * bf16 only (RGC_ERR_DTYPE otherwise); D must be 64, the head dim of each
- * map in the differential workload (RGC_ERR_HEADDIM otherwise); kv_ss in
- * [0, 2^24) elements (RGC_ERR_LAYOUT otherwise).  Each map's weights are
- * summed in fp32 and rounded to bf16 where they multiply V; o is rounded
- * once from fp32.  A row whose
- * slots fall outside the cache gets NaN and raises *err_flag.
+ * bf16 only (RGC_ERR_DTYPE otherwise); head dim 32, 64 or 128
+ * (RGC_ERR_HEADDIM otherwise); kv_ss in [0, 2^24) elements (RGC_ERR_LAYOUT
+ * otherwise).  Each map's weights are summed in fp32 and rounded to bf16
+ * where they multiply V.  At head dim 64 (each map's head dim in the
+ * differential workload) one kernel forms both maps and o is rounded once
+ * from fp32.  At 32 and 128 the call is two launches of the causal prefill
+ * on the stream: o = the first map's output (rounded to bf16), then o plus
+ * -lambda times the second map's output (rounded to bf16), added in fp32
+ * and rounded once more; with lambda = 0 the result is bit for bit that of
+ * rgc_gqa_attn_prefill on (q1, K1, V).  A row whose slots fall outside the
+ * cache gets NaN and raises *err_flag.
  */
 int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2,
                           const void* k1_cache, const void* k2_cache,

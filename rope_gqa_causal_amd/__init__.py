@@ -352,7 +352,7 @@ def diff_attn_prefill(q1, q2, k1_cache, k2_cache, v_cache, lam, q_start=None, sc
     """Causal differential GQA: (softmax(q1 K1^T) - lam softmax(q2 K2^T)) V.
 
     q1, q2 [B,Sq,Hq,D] (same strides); caches [B,Hkv,S_max,D] (same strides);
-    bf16, D = 64."""
+    bf16, D in {32, 64, 128}."""
     _gpu(q1, q2, k1_cache, k2_cache, v_cache, q_start, out, err_flag)
     B, Sq, Hq, D = q1.shape
     _, Hkv, S_max, _ = k1_cache.shape

@@ -371,7 +371,6 @@ int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2, const void* k
   int st = check_attn_common(dtype, B, Sq, Hq, Hkv, D, S_max);
   if (st != RGC_OK) return st;
   if (dtype != RGC_BF16) return RGC_ERR_DTYPE;
-  if (D != 64) return RGC_ERR_HEADDIM;
   if (B == 0 || Sq == 0) return RGC_OK;
   if (!o || !q1 || !q2 || !k1_cache || !k2_cache || !v_cache) return RGC_ERR_NULL;
   if (Sq > S_max) return RGC_ERR_CAPACITY;
@@ -415,7 +414,19 @@ int rgc_diff_attn_prefill(void* o, const void* q1, const void* q2, const void* k
   dp.q2 = q2;
   dp.k2 = k2_cache;
   dp.lambda = lambda;
-  return hip_status(launch_diff_bf16(dp, reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (D == 64) return hip_status(launch_diff_bf16(dp, s));
+  // Other head dims: the two maps' outputs are linear in V, so o is the
+  // causal prefill of (q1, K1, V), then the prefill of (q2, K2, V) added
+  // with weight -lambda in its epilogue (two launches on the stream).
+  hipError_t e = launch_prefill_bf16(p, s);
+  if (e != hipSuccess) return hip_status(e);
+  AttnParams p2 = p;
+  p2.q = q2;
+  p2.k = k2_cache;
+  p2.out_add = 1;
+  p2.out_add_scale = -lambda;
+  return hip_status(launch_prefill_bf16(p2, s));
 }
 
 size_t rgc_diff_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_len) {

@@ -102,6 +102,8 @@ struct AttnParams {
   float scale;
   float* lse;               // [B,Hq,Sq] or NULL
   int32_t* err;
+  int out_add;              // bf16 prefill: 0 stores o; 1 adds out_add_scale * (this pass's o) to o
+  float out_add_scale;
 };
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, bool decode, hipStream_t stream);

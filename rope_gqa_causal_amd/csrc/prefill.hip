@@ -380,7 +380,9 @@ __device__ __forceinline__ void tile_step(WaveCtx<D>& w, const Stager<D>& sg, ui
 // wave of the workgroup runs it and passes the same barriers, so items
 // chain in a persistent workgroup; an item that needs no work (rows past a
 // document's end, a capacity violation) is skipped by the whole workgroup.
-template <int D>
+// ADD: the epilogue adds p.out_add_scale times this pass's o to o (an
+// instantiation of its own, so the plain prefill's code is untouched).
+template <int D, bool ADD>
 __device__ __forceinline__ void run_item(const AttnParams& p, char* lds, int group, int b, int kvh, int rb,
                                          int tid, int lane, int wave) {
   using T = Tile<D>;
@@ -552,7 +554,20 @@ __device__ __forceinline__ void run_item(const AttnParams& p, char* lds, int gro
         const int pr = Rr / group, hr = kvh * group + Rr % group;
         bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (int64_t)b * p.o_sb + (tok0 + pr) * p.o_ss +
                        (int64_t)hr * p.o_sh;
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(orow + 8 * c));
+        if constexpr (ADD) {
+          // o += scale * (this pass's o), in fp32, rounded once (the
+          // second pass of a differential attention at head dims the fused
+          // differential kernel does not take).
+          const u32x4 old = ld16(orow + 8 * c);
+          u32x4 sum;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sum[e] = pack_bf16x2(fmaf(p.out_add_scale, bf16_lo(v[e]), bf16_lo(old[e])),
+                                 fmaf(p.out_add_scale, bf16_hi(v[e]), bf16_hi(old[e])));
+          st16(orow + 8 * c, sum);
+        } else {
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(orow + 8 * c));
+        }
       }
     }
     if (col_ok && p.lse && half == 0) p.lse[lse_base + pos] = (w.m_run + log2f(lsum)) * kLn2;
@@ -575,7 +590,7 @@ __device__ __forceinline__ void run_item(const AttnParams& p, char* lds, int gro
 //    n-1..0, ...), which evens out the sums of their tile counts; the
 //    workgroups never leave the compute unit, so no item waits for a
 //    workgroup launch.
-template <int D>
+template <int D, bool ADD>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int nrb, int persistent) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int group = p.Hq / p.Hkv;
@@ -595,7 +610,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(AttnParams p, int 
     const int gi = k / (G * nrb), g0 = gi * G, gn = min(G, cnt - g0);
     const int kk = k - gi * G * nrb;
     const int u = x + kXcds * (g0 + kk % gn);
-    run_item<D>(p, lds, group, u / p.Hkv, u % p.Hkv, nrb - 1 - kk / gn, tid, lane, wave);
+    run_item<D, ADD>(p, lds, group, u / p.Hkv, u % p.Hkv, nrb - 1 - kk / gn, tid, lane, wave);
   }
 }
 
@@ -626,8 +641,12 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   const bool persistent = !p.cu_seqlens && cus > 0 && total > cus;
   const unsigned grid = persistent ? (unsigned)cus : (unsigned)total;
   KernelTimer kt_("prefill_kernel", stream);
-  hipLaunchKernelGGL(prefill_kernel<D>, dim3(grid), dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream, p, nrb,
-                     persistent ? 1 : 0);
+  if (p.out_add)
+    hipLaunchKernelGGL((prefill_kernel<D, true>), dim3(grid), dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream, p,
+                       nrb, persistent ? 1 : 0);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(grid), dim3(kThreads), (size_t)Tile<D>::LDS_BYTES, stream,
+                       p, nrb, persistent ? 1 : 0);
   return hipGetLastError();
 }
 

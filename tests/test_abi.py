@@ -85,7 +85,7 @@ def _diff(**kw):
 def test_diff_rejects_bad_arguments_before_launch():
     assert _diff(Hq=3) == GROUP
     assert _diff(dt=F32) == DTYPE        # bf16 only
-    assert _diff(D=128) == HEADDIM       # head dim 64 only
+    assert _diff(D=96) == HEADDIM        # head dims 32, 64, 128
     assert _diff(q2=None) == NULL
     assert _diff(k2=A + 8) == LAYOUT
     assert _diff(kv_ss=1 << 24) == LAYOUT

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 D = 64
 
 
-def _diff_case(B, Sq, Hq, Hkv, q_start, S_max, seed):
+def _diff_case(B, Sq, Hq, Hkv, q_start, S_max, seed, D=D):
     g = synth.generator(seed)
     q1 = synth.normal((B, Sq, Hq, D), g)
     q2 = synth.normal((B, Sq, Hq, D), g)
@@ -94,3 +94,32 @@ def test_diff_capacity_violation_gives_nan_rows_and_a_flag():
     o = rgc.diff_attn_prefill(q1.cuda(), q2.cuda(), k1.cuda(), k2.cuda(), v.cuda(), 0.8, bad, err_flag=err)
     assert err.item() == 1
     assert torch.isnan(o[1].float()).all() and torch.isfinite(o[0].float()).all()
+
+
+# Head dims other than 64 run as two launches of the causal prefill kernel,
+# the second adding -lambda times its output into o.
+TWO_PASS_CASES = [
+    # D, B, Sq, Hq, Hkv, q_start, S_max, lambda
+    (128, 2, 300, 6, 2, [0, 0], 300, 0.8),    # g=3, ragged tail
+    (128, 2, 77, 4, 4, [500, 31], 600, 0.8),  # rows start mid-cache
+    (32, 1, 257, 8, 2, [0], 260, 1.25),       # g=4, lambda above one
+    (32, 3, 1, 4, 2, [0, 9, 100], 128, 0.5),  # single rows
+]
+
+
+@pytest.mark.parametrize("case", TWO_PASS_CASES, ids=lambda c: f"D{c[0]}B{c[1]}Sq{c[2]}H{c[3]}/{c[4]}")
+def test_diff_attn_two_pass_head_dims(case):
+    Dh, B, Sq, Hq, Hkv, q_start, S_max, lam = case
+    q1, q2, k1, k2, v, qs = _diff_case(B, Sq, Hq, Hkv, q_start, S_max, Sq + Hq + Dh, D=Dh)
+    print(f"[diff two-pass] D={Dh} B={B} Sq={Sq} H={Hq}/{Hkv}", flush=True)
+    ref = oracle.diff_attn(q1, q2, k1, k2, v, lam, qs)
+    g = [t.cuda() for t in (q1, q2, k1, k2, v)]
+    o = rgc.diff_attn_prefill(g[0], g[1], g[2], g[3], g[4], lam, qs.cuda())
+    torch.cuda.synchronize()
+    assert_close(o, ref, torch.bfloat16, f"diff attention, D {Dh}")
+    # lambda = 0 leaves the first pass's output untouched: bit for bit the
+    # causal prefill of (q1, K1, V).
+    zero = rgc.diff_attn_prefill(g[0], g[1], g[2], g[3], g[4], 0.0, qs.cuda())
+    plain = rgc.gqa_attn_prefill(g[0], g[2], g[4], qs.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(zero.view(torch.int16), plain.view(torch.int16))
